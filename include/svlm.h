@@ -1,0 +1,225 @@
+/*
+ * svlm.h - C ABI of libsvlm: the data-parallel hot path of verifier-guided
+ * visual-token / KV selection and draft/verify decode attention for lossless
+ * speculative decoding of video LLMs, written for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [SpecVLM-5]  SpecVLM, Zhejiang University technology-transfer listing,
+ *                section 5 "solution": text-to-visual mean attention from the
+ *                target; two-stage pruning (Top-P by attention share, then a
+ *                spatially uniform pick of the low-attention rest).
+ *   [SpecVLM-A]  SpecVLM abstract (arXiv 2508.16201): verifier-guided stage I,
+ *                spatially uniform stage II, up to 90% of video tokens pruned.
+ *   [StD-dec]    Sparse-to-Dense explainer (arXiv 2505.19155), technical
+ *                summary, "decoding process": gamma drafted tokens, verified by
+ *                the dense model in one I/O pass over the full KV cache; longest
+ *                matching prefix plus one bonus token.
+ *   [StD-sel]    Same page, "KV cache selection": top-K visual KV picked at
+ *                prefill from mean text-to-visual attention, per layer and head;
+ *                "dual-module architecture": the sparse draft reads only the
+ *                selected KV.
+ *   [PVLM-PD]    ParallelVLM notes (CVPR 2026), background and "parallel
+ *                decoding": candidates accepted by rejection sampling, which
+ *                keeps the target's output distribution; a rejected token is
+ *                resampled from the target.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless a parameter says otherwise.  Sizes
+ *     and strides are in ELEMENTS of the pointed-to type.  The caller owns all
+ *     buffers; the library never allocates or frees device memory and keeps no
+ *     state between calls (apart from a per-device property cache).
+ *   - Everything is enqueued on `stream` (a hipStream_t passed as void*; NULL
+ *     is the default stream).  Calls return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     bad argument nothing is enqueued, a status is returned and
+ *     svlm_last_error() gives a text (thread-local).  SVLM_E_HIP reports a
+ *     launch error from the HIP runtime (including an earlier asynchronous
+ *     fault surfacing at this launch).
+ *   - Device data that the host cannot see (indices, lengths, scores) are
+ *     preconditions, stated per call; kernels clamp them so that no access
+ *     leaves the buffers, but results are unspecified when they are violated.
+ *   - Only D in {64, 128} and bf16 (SVLM_BF16) attention operands are
+ *     supported; the innermost (D) dimension must be contiguous and every
+ *     row 16-byte aligned.
+ *   - Selection, gather and acceptance are bit-deterministic; score and
+ *     attention are run-to-run deterministic (fixed reduction order).
+ *   - Calls on different streams may run concurrently if their workspaces
+ *     differ.
+ */
+#ifndef SVLM_H
+#define SVLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVLM_ABI_VERSION 1
+
+enum svlm_status {
+  SVLM_OK = 0,
+  SVLM_E_INVALID = 1,     /* an argument is out of range, null or misaligned */
+  SVLM_E_UNSUPPORTED = 2, /* a valid request this build does not implement (dtype, D) */
+  SVLM_E_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace() size */
+  SVLM_E_HIP = 4          /* the HIP runtime reported an error */
+};
+
+enum svlm_dtype { SVLM_BF16 = 0, SVLM_F32 = 1 };
+enum svlm_agg { SVLM_AGG_QHEAD = 0, SVLM_AGG_KVHEAD = 1, SVLM_AGG_ALL = 2 };
+enum svlm_verify_mode { SVLM_VERIFY_GREEDY = 0, SVLM_VERIFY_REJECT = 1 };
+
+/* ABI version of the loaded library (SVLM_ABI_VERSION at build time). */
+int svlm_abi_version(void);
+/* Static text for a status code. */
+const char* svlm_status_string(int status);
+/* Thread-local text describing the last failure of a call on this thread. */
+const char* svlm_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * svlm_score - mean text-to-visual softmax attention of one layer.
+ * [SpecVLM-5]; [StD-sel].
+ *
+ * For q head h (KV head g = h / (Hq/Hkv)), text query t at position
+ * q_pos0 + t sees keys 0..q_pos0+t (causal) of k:
+ *     P[t,h,n] = softmax_n(scale * <q_text[t,h], k[g,n]>)
+ *     A[h,i]   = (1/T) * sum_t P[t,h,vis_start+i],   i < n_vis
+ * The softmax runs over the whole visible range; visual columns are read
+ * out of the normalised rows.  Aggregation `agg`: SVLM_AGG_QHEAD -> rows
+ * [Hq][n_vis]; SVLM_AGG_KVHEAD -> mean over each group, [Hkv][n_vis];
+ * SVLM_AGG_ALL -> mean over all q heads, [1][n_vis].  Then
+ *     out = alpha * agg(A) + beta * out        (beta == 0: out is not read)
+ * which lets several layers be averaged into one row set.
+ *
+ * q_text: [T][Hq][D] bf16 with strides q_st (per text token) and q_sh (per
+ *         head); D contiguous.
+ * k:      [Hkv][n_ctx][D] bf16 with strides k_sh, k_sn.
+ * out:    fp32 rows, contiguous [rows][n_vis].
+ * ws:     svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis) bytes (per-split row
+ *         statistics and per-head score rows).
+ * Requires 1 <= T <= 128, scale > 0, q_pos0 + T <= n_ctx, 0 <= vis_start, vis_start + n_vis
+ * <= q_pos0 + 1 (every visual key visible to every text query).
+ * Computes QK^T on bf16 matrix cores with fp32 accumulation, in two passes
+ * (row log-sum-exp, then normalised column sums); the score matrix is never
+ * stored.
+ * ------------------------------------------------------------------------ */
+size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis);
+int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh,
+               const void* k, int64_t k_sh, int64_t k_sn,
+               int dtype, int T, int n_ctx, int q_pos0, int vis_start, int n_vis,
+               int Hq, int Hkv, int D, float scale, int agg,
+               float alpha, float beta, float* out,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_select - two-stage visual token selection, one row at a time.
+ * [SpecVLM-5] (stages i and ii); [SpecVLM-A]; [StD-sel] for top_p >= 1.
+ *
+ * Each row holds n_vis = F*H*W fp32 scores s in [0, 1] (precondition),
+ * token n = f*H*W + y*W + x (frame-major raster order).
+ * Order: score descending, then index ascending.  Mass of a token:
+ * floor(s * 2^40) as an exact integer; row total Q; target
+ * ceil(double(Q) * top_p) in IEEE round-to-nearest double arithmetic.
+ * Stage I keeps the shortest top prefix whose mass reaches the target,
+ * truncated to `budget` tokens (top_p >= 1: the top `budget`; top_p <= 0:
+ * none).  k1 = its size.  Stage II walks the other n_rem = n_vis - k1 tokens
+ * in raster order and keeps the ones at ranks floor((2j+1)*n_rem/(2m)),
+ * j < m = budget - k1 (one constant stride with centred phase, so each frame
+ * gets its share spread evenly over its H x W grid).
+ *
+ * scores:   [R] rows with stride row_stride.
+ * kept:     [R][budget] int32, ascending token indices (output).
+ * n_stage1: [R] int32 k1 (output).  tag: [R][n_vis] uint8 or NULL
+ *           (0 dropped, 1 stage I, 2 stage II).
+ * ws:       svlm_select_workspace(R, n_vis) bytes.
+ * Requires 0 <= budget <= n_vis <= 2^18.
+ * ------------------------------------------------------------------------ */
+size_t svlm_select_workspace(int R, int n_vis);
+int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, int W,
+                double top_p, int budget, int32_t* kept, int32_t* n_stage1, uint8_t* tag,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_gather_kv - compact the kept KV rows into a draft cache.
+ * [StD-sel] ("dual-module architecture": the draft reads only selected KV).
+ *
+ * For every KV head g:
+ *   dst[g, j]         = src[g, idx[g*idx_sh + j]],   j < n_idx
+ *   dst[g, n_idx + j] = src[g, tail_start + j],      j < n_tail
+ * (the tail carries the always-kept text rows).  Applied to K and V alike.
+ * src: [Hkv][n_src][D] with strides s_sh, s_sn; dst: strides d_sh, d_sn.
+ * idx_sh = 0: one list for all heads; otherwise per-head lists.
+ * Indices outside [0, n_src) are a precondition violation; such rows are
+ * written as zeros.  Requires tail_start + n_tail <= n_src.  With
+ * n_idx + n_tail == 0 nothing is done (pointers may be NULL).
+ * ------------------------------------------------------------------------ */
+int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s_sn, int n_src,
+                   const int32_t* idx, int64_t idx_sh, int n_idx, int tail_start, int n_tail,
+                   void* k_dst, void* v_dst, int64_t d_sh, int64_t d_sn,
+                   int Hkv, int D, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_decode_attn - split-K grouped-query decode attention, draft or verify.
+ * [StD-dec] (sparse draft over the kept KV, one query; dense verify of the
+ * gamma+1 newest tokens in one pass over the full KV); [SpecVLM-5] / page 1
+ * section 4 (decode is bound by loading the KV cache every step).
+ *
+ * For batch b, query i < nq and q head h (g = h / (Hq/Hkv)), keys
+ * n < L(b,i) with L = kv_len[b] - nq + i + 1 if causal_tail else kv_len[b]:
+ *   out[b,i,h] = sum_n softmax_n(scale*<q[b,i,h], k[b,g,n]>) * v[b,g,n]
+ *   lse[b,i,h] = log sum_n exp(scale*<q[b,i,h], k[b,g,n]>)   (natural log)
+ * q:   [B][nq][Hq][D] bf16, batch stride q_sb, the rest contiguous.
+ * k,v: [B][Hkv][max_kv_len][D] bf16 with strides kv_sb, kv_sh, kv_sn.
+ * kv_len: [B] int32 on the device; precondition nq <= kv_len[b] <=
+ *         max_kv_len (values are clamped into [0, max_kv_len]).
+ * out: [B][nq][Hq][D] fp32 contiguous; lse: [B][nq][Hq] fp32 or NULL.
+ * num_splits: key-range splits per (batch, KV head); 0 picks one for the
+ *   chip.  With more than one split the partial (max, sum, output) states go
+ *   to ws and are merged in a fixed order.
+ * ws: svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits)
+ *   bytes (0 when one split suffices).
+ * Works in bf16 matrix-core products with fp32 accumulation; the softmax
+ * weights enter the value product as a bf16 hi + lo pair, so the output
+ * keeps fp32-level accuracy.
+ * ------------------------------------------------------------------------ */
+size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len,
+                                  int num_splits);
+int svlm_decode_attn(const void* q, int64_t q_sb,
+                     const void* k, const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                     const int32_t* kv_len, int max_kv_len,
+                     int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                     int causal_tail, float* out, float* lse,
+                     int num_splits, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_verify - acceptance of gamma drafted tokens.
+ * SVLM_VERIFY_GREEDY [StD-dec]: a_i = argmax target[b,i,:] (lowest index on
+ *   ties); n = length of the longest prefix with draft_tok[b,j] == a_j;
+ *   next_tok = a_n (a correction when n < gamma, the bonus token when
+ *   n == gamma).  target holds logits [B][gamma+1][V].
+ * SVLM_VERIFY_REJECT [PVLM-PD], standard speculative sampling: target holds
+ *   probabilities p [B][gamma+1][V], draft_prob q [B][gamma][V], u
+ *   [B][gamma+1] uniforms in [0,1).  Token i is accepted iff
+ *   u_i * q_i(d_i) <= p_i(d_i) (exact fp64 product); at the first rejection
+ *   n = i and next_tok is drawn from max(0, p_i - q_i) (formed in fp32);
+ *   if all are accepted n = gamma and next_tok is drawn from p_gamma.  The
+ *   draw is a fixed-point inverse CDF with u_gamma: m_v = floor(w_v*2^40),
+ *   W = sum m_v, t = min(floor(double(u)*double(W)), W-1), token = least v
+ *   with m_0+..+m_v > t.  If W == 0 the draw uses p_i instead, then
+ *   argmax p_i.
+ * n_accept, next_tok: [B] int32 outputs.  Requires 1 <= gamma, 1 <= V,
+ * draft tokens in [0, V) (clamped otherwise), probabilities in [0, 1].
+ * ws: svlm_verify_workspace(batch, gamma, V) bytes.
+ * ------------------------------------------------------------------------ */
+size_t svlm_verify_workspace(int batch, int gamma, int V);
+int svlm_verify(int mode, int batch, int gamma, int V, const int32_t* draft_tok,
+                const float* target, const float* draft_prob, const float* u,
+                int32_t* n_accept, int32_t* next_tok,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVLM_H */

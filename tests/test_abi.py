@@ -1,0 +1,98 @@
+"""The C ABI library loads and exports every symbol include/svlm.h declares;
+host-side validation rejects bad arguments before touching a device."""
+import ctypes as C
+import os
+
+import pytest
+
+from tests._util import declared_symbols
+from visual_kv_pruning_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libsvlm.so is not built (run python -m visual_kv_pruning_amd.build)")
+    return L.load()
+
+
+def test_header_declares_the_five_calls():
+    syms = declared_symbols()
+    for name in ("svlm_score", "svlm_select", "svlm_gather_kv", "svlm_decode_attn", "svlm_verify"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for name in syms:
+        assert hasattr(lib, name), name
+        assert name in L.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.svlm_abi_version() == 1
+    for st in range(5):
+        assert lib.svlm_status_string(st)
+    assert b"unknown" in lib.svlm_status_string(99)
+
+
+def test_workspace_queries_are_host_only(lib):
+    assert lib.svlm_select_workspace(4, 1000) == 0
+    assert lib.svlm_verify_workspace(1, 5, 152064) > 0
+    assert lib.svlm_verify_workspace(0, 5, 10) == 0
+
+
+NULL = None
+
+
+def _attn(lib, **kw):
+    args = dict(q=NULL, q_sb=0, k=NULL, v=NULL, kv_sb=0, kv_sh=0, kv_sn=128, kv_len=NULL, max_kv_len=10,
+                dtype=L.SVLM_BF16, batch=1, nq=1, Hq=8, Hkv=2, D=128, scale=0.1, causal=0, out=NULL, lse=NULL,
+                num_splits=0, ws=NULL, ws_bytes=0, stream=NULL)
+    args.update(kw)
+    return lib.svlm_decode_attn(*args.values())
+
+
+def test_decode_attn_rejects_bad_arguments(lib):
+    fake = C.c_void_p(4096)   # never dereferenced: validation fails first
+    ok = dict(q=fake, k=fake, v=fake, kv_len=fake, out=fake)
+    assert _attn(lib, D=96, **ok) == L.SVLM_E_UNSUPPORTED
+    assert _attn(lib, dtype=L.SVLM_F32, **ok) == L.SVLM_E_UNSUPPORTED
+    assert _attn(lib) == L.SVLM_E_INVALID                              # null pointers
+    assert _attn(lib, Hq=6, Hkv=4, **ok) == L.SVLM_E_INVALID          # Hq % Hkv
+    assert _attn(lib, nq=0, **ok) == L.SVLM_E_INVALID
+    assert _attn(lib, scale=float("inf"), **ok) == L.SVLM_E_INVALID
+    assert _attn(lib, causal=2, **ok) == L.SVLM_E_INVALID
+    assert _attn(lib, kv_sn=100, **ok) == L.SVLM_E_INVALID            # row stride not a multiple of 8
+    assert _attn(lib, q=C.c_void_p(4098), k=fake, v=fake, kv_len=fake, out=fake) == L.SVLM_E_INVALID  # misaligned
+    assert b"16-byte" in lib.svlm_last_error()
+
+
+def test_verify_select_gather_score_reject_bad_arguments(lib):
+    fake = C.c_void_p(4096)
+    assert lib.svlm_verify(7, 1, 1, 10, fake, fake, fake, fake, fake, fake, fake, 1 << 20, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_verify(0, 1, 0, 10, fake, fake, fake, fake, fake, fake, fake, 1 << 20, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_verify(1, 1, 2, 10, fake, fake, NULL, fake, fake, fake, fake, 1 << 20, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_verify(0, 1, 2, 10, fake, fake, NULL, NULL, fake, fake, NULL, 0, NULL) == L.SVLM_E_WORKSPACE
+    # select: budget beyond n_vis, bad grid, too long rows
+    assert lib.svlm_select(fake, 20, 1, 2, 2, 5, 0.5, 21, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_select(fake, 20, 1, 0, 2, 5, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_select(fake, 1 << 20, 1, 1024, 16, 17, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_UNSUPPORTED
+    assert lib.svlm_select(fake, 20, 1, 2, 2, 5, float("nan"), 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_select(fake, 10, 1, 2, 2, 5, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID  # stride
+    # gather: tail past the source, unsupported D
+    assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 8, 3, fake, fake, 0, 128, 1, 128, 0, NULL) == L.SVLM_E_INVALID
+    assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 0, 3, fake, fake, 0, 128, 1, 80, 0, NULL) == L.SVLM_E_UNSUPPORTED
+    # score: T too large, visual range beyond what text sees, non-positive scale
+    args = [fake, 1024, 128, fake, 1 << 16, 128, 0, 200, 300, 100, 0, 50, 8, 2, 128, 0.1, 2, 1.0, 0.0, fake, fake, 1 << 20, NULL]
+    assert lib.svlm_score(*args) == L.SVLM_E_UNSUPPORTED
+    args[7] = 16
+    args[11] = 150
+    assert lib.svlm_score(*args) == L.SVLM_E_INVALID
+    args[11] = 50
+    args[15] = -0.1
+    assert lib.svlm_score(*args) == L.SVLM_E_INVALID
+    args[15] = 0.1
+    args[16] = 9
+    assert lib.svlm_score(*args) == L.SVLM_E_INVALID

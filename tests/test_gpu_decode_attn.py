@@ -1,0 +1,147 @@
+"""Decode attention (draft and dense verify) on the GPU vs the fp64 oracle.
+
+Tolerance: per (query, head) row, max_d |o - o_ref| / max_d |o_ref| <= 2e-3
+(bf16 inputs, fp32 accumulation); lse within 1e-3 absolute."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests._util import dev_bf16, log, row_rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+torch = pytest.importorskip("torch")
+
+
+def _run(q, k, v, kv_len, causal, num_splits=0):
+    from visual_kv_pruning_amd import ops
+    qd = dev_bf16(q)
+    kd = dev_bf16(k)
+    vd = dev_bf16(v)
+    kl = torch.tensor(np.asarray(kv_len, np.int32), device="cuda:0")
+    o, lse = ops.decode_attn(qd, kd, vd, kl, causal, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(q, k, v, kv_len, causal, num_splits=0, name=""):
+    log(f"decode_attn case {name}: q{q.shape} k{k.shape} kv_len={list(kv_len)} causal={causal} splits={num_splits}")
+    o, lse = _run(q, k, v, kv_len, causal, num_splits)
+    ro, rl = oracle.decode_attn(q, k, v, kv_len, causal)
+    err = row_rel_err(o, ro)
+    lerr = float(np.abs(lse - rl).max())
+    log(f"  row-rel err {err:.2e}  lse err {lerr:.2e}")
+    assert err <= TOL, name
+    assert lerr <= 1e-3, name
+    return o, lse
+
+
+def _rand(seed, *shape):
+    rng = np.random.default_rng(seed)
+    return W.bf16_round(rng.standard_normal(shape).astype(np.float32))
+
+
+def test_tiny_config_verify_and_draft():
+    cfg = W.C1
+    p = W.prefill_layer(cfg, 0)
+    nq = cfg.gamma_verify + 1
+    kn, vn = W.new_kv(cfg, 0, nq)
+    k = np.concatenate([p.k, kn], axis=1)
+    v = np.concatenate([p.v, vn], axis=1)
+    q = W.decode_queries(cfg, 0, nq)
+    _check(q, k, v, [k.shape[1]], True, name="tiny verify")
+    # draft over the kept visual rows + text + the newest token
+    kept = np.sort(np.random.default_rng(0).choice(cfg.n_vis, cfg.budget, replace=False))
+    rows = np.concatenate([kept, np.arange(cfg.n_vis, k.shape[1] - nq + 1)])
+    _check(q[:, :1], k[:, rows], v[:, rows], [len(rows)], False, name="tiny draft")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,nq", [(1, 1), (2, 5), (5, 10), (7, 1), (8, 6), (8, 1)])
+@pytest.mark.parametrize("N", [1, 31, 33, 65, 1000, 4099])
+def test_shapes_and_ragged_tails(D, G, nq, N):
+    if N < nq:
+        pytest.skip("fewer keys than new queries")
+    Hkv = 2
+    Hq = G * Hkv
+    seed = D * 100000 + G * 1000 + nq * 100 + N
+    q = _rand(seed, 1, nq, Hq, D)
+    k = _rand(seed + 1, Hkv, N, D)
+    v = _rand(seed + 2, Hkv, N, D)
+    _check(q, k, v, [N], nq > 1, name=f"D{D} G{G} nq{nq} N{N}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])
+def test_forced_split_counts_agree(splits):
+    q = _rand(7, 1, 6, 16, 128)
+    k = _rand(8, 2, 3000, 128)
+    v = _rand(9, 2, 3000, 128)
+    _check(q, k, v, [3000], True, num_splits=splits, name=f"splits={splits}")
+
+
+def test_batch_with_ragged_lengths_and_strided_cache():
+    B, nq, Hq, Hkv, D, Ncap = 3, 4, 8, 2, 128, 700
+    q = _rand(11, B, nq, Hq, D)
+    k = _rand(12, B, Hkv, Ncap, D)
+    v = _rand(13, B, Hkv, Ncap, D)
+    kv_len = [700, 333, 4]
+    log("decode_attn case batch ragged")
+    o, lse = _run(q, k, v, kv_len, True)
+    for b in range(B):
+        ro, rl = oracle.decode_attn(q[b:b + 1], k[b], v[b], [kv_len[b]], True)
+        assert row_rel_err(o[b:b + 1], ro) <= TOL
+        assert np.abs(lse[b:b + 1] - rl).max() <= 1e-3
+
+
+def test_verify_equals_sequential_draft_calls_on_gpu():
+    """One dense pass over nq queries == nq single-query calls on the prefixes (same kernel family)."""
+    nq, Hq, Hkv, D, N = 6, 16, 2, 128, 2500
+    q = _rand(21, 1, nq, Hq, D)
+    k = _rand(22, Hkv, N, D)
+    v = _rand(23, Hkv, N, D)
+    o, _ = _run(q, k, v, [N], True)
+    for i in range(nq):
+        n_i = N - nq + i + 1
+        oi, _ = _run(q[:, i:i + 1], k[:, :n_i], v[:, :n_i], [n_i], False)
+        assert row_rel_err(o[:, i:i + 1], oi) <= 1e-4
+
+
+def test_deterministic_across_runs():
+    q = _rand(31, 1, 6, 64, 128)
+    k = _rand(32, 8, 5000, 128)
+    v = _rand(33, 8, 5000, 128)
+    a, la = _run(q, k, v, [5000], True)
+    b, lb = _run(q, k, v, [5000], True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_llava72b_shape_verify_and_draft_full_size():
+    """72B shape at full size: 64 q / 8 KV heads, 25088 visual + 128 text + 6 verify tokens."""
+    cfg = W.C3
+    nq = cfg.gamma_verify + 1
+    N = cfg.n_ctx + nq
+    k, v = W.random_kv(cfg.index, cfg.hkv, N, cfg.d, layer=0)
+    q = W.decode_queries(cfg, 0, nq)
+    _check(q, k, v, [N], True, name="72B verify (launch used by the bench)")
+    # 10% draft: kept visual + text + newest
+    nk = cfg.budget + cfg.n_text + 1
+    _check(q[:, :1], k[:, :nk], v[:, :nk], [nk], False, name="72B draft")
+
+
+def test_hour_long_shape_verify_sampled_heads():
+    """141,194-key dense verify at the hour-long shape; oracle on the first KV head's rows."""
+    cfg = W.C5
+    nq = cfg.gamma_verify + 1
+    N = cfg.n_ctx + nq
+    k, v = W.random_kv(cfg.index, cfg.hkv, N, cfg.d, layer=0)
+    q = W.decode_queries(cfg, 0, nq)
+    log("decode_attn case hour-long verify")
+    o, lse = _run(q, k, v, [N], True)
+    G = cfg.group
+    ro, rl = oracle.decode_attn(q[:, :, :G], k[:1], v[:1], [N], True)
+    assert row_rel_err(o[:, :, :G], ro) <= TOL
+    assert np.abs(lse[:, :, :G] - rl).max() <= 1e-3

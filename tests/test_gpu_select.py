@@ -1,0 +1,69 @@
+"""Selection on the GPU vs the oracle: bit-exact kept lists, stage-I counts and tags
+when both sides see the same fp32 scores."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests._util import log
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _gpu_select(rows, F, H, Wd, top_p, budget):
+    from visual_kv_pruning_amd import ops
+    s = torch.from_numpy(np.ascontiguousarray(rows, np.float32)).to("cuda:0")
+    kept, n1, tag = ops.select(s, F, H, Wd, top_p, budget, with_tag=True)
+    torch.cuda.synchronize()
+    return kept.cpu().numpy(), n1.cpu().numpy(), tag.cpu().numpy()
+
+
+def _check(rows, F, H, Wd, top_p, budget, name):
+    log(f"select case {name}: R={rows.shape[0]} N={rows.shape[1]} P={top_p} B={budget}")
+    kept, n1, tag = _gpu_select(rows, F, H, Wd, top_p, budget)
+    rk, r1, rt = oracle.select_rows(rows, F, H, Wd, top_p, budget)
+    assert np.array_equal(n1, r1), name
+    assert np.array_equal(kept, rk.astype(np.int32)), name
+    assert np.array_equal(tag, rt), name
+
+
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+@pytest.mark.parametrize("top_p", [0.0, 0.1, 0.5, 0.6, 1.0])
+def test_heavy_tailed_rows(kind, top_p):
+    F, H, Wd = 8, 14, 14
+    N = F * H * Wd
+    rows = W.score_rows(kind, 3, N, seed=5)
+    _check(rows, F, H, Wd, top_p, int(math.ceil(0.1 * N)), f"{kind}")
+
+
+@pytest.mark.parametrize("budget", [0, 1, 7, 196, 700, 1567, 1568])
+def test_budget_edges(budget):
+    F, H, Wd = 8, 14, 14
+    rows = W.score_rows("lognormal2", 2, F * H * Wd, seed=6)
+    _check(rows, F, H, Wd, 0.5, budget, f"budget={budget}")
+
+
+def test_golden_worked_example():
+    s = np.array([4, 0, 1, 8, 2, 2, 0, 3, 16, 1, 2, 1], np.float32) / np.float32(64)
+    for p, b in ((0.5, 5), (0.9, 5), (0.0, 4), (1.0, 4), (0.3, 5)):
+        _check(s[None], 2, 2, 3, p, b, f"golden P={p}")
+
+
+@pytest.mark.parametrize("cfg", [W.C1, W.C2, W.C3, W.C4, W.C5], ids=lambda c: c.name)
+def test_config_shapes(cfg):
+    """Each configuration's row length, budget and Top-P, on heavy-tailed and flat rows."""
+    R = {"all": 1, "layer": 4, "layer_kvhead": 6}[cfg.rows]
+    for kind in ("lognormal3", "flat", "pareto1.1"):
+        rows = W.score_rows(kind, R, cfg.n_vis, seed=cfg.index)
+        _check(rows, cfg.frames, cfg.gh, cfg.gw, cfg.top_p, cfg.budget, f"{cfg.name}/{kind}")
+
+
+def test_scores_from_the_value_model():
+    """Rows from the oracle's own score of the tiny configuration (nearly flat attention)."""
+    cfg = W.C1
+    p = W.prefill_layer(cfg, 0)
+    row = oracle.aggregate_heads(oracle.score_layer(p.q_text, p.k, p.q_pos0, 0, cfg.n_vis, cfg.hkv), cfg.hkv, "all")
+    _check(row.astype(np.float32), cfg.frames, cfg.gh, cfg.gw, cfg.top_p, cfg.budget, "tiny value model")

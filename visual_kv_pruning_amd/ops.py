@@ -1,0 +1,191 @@
+"""Thin PyTorch-facing wrappers over the libsvlm C ABI.
+
+Each function checks devices, dtypes and shapes, allocates outputs and
+workspaces with torch (device memory only), and calls the matching svlm_*
+entry point on torch's current stream.  Every step of the computation runs
+in the HIP kernels; nothing here computes on tensors.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as L
+
+_AGG = {"qhead": L.SVLM_AGG_QHEAD, "kvhead": L.SVLM_AGG_KVHEAD, "all": L.SVLM_AGG_ALL}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("svlm tensors must live on the GPU")
+
+
+def _bf16(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"expected bfloat16, got {t.dtype}")
+        if t.stride(-1) != 1:
+            raise ValueError("the last (head-dim) axis must be contiguous")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def score_workspace_bytes(T: int, Hq: int, Hkv: int, q_pos0: int, n_vis: int) -> int:
+    return int(L.load().svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis))
+
+
+def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_start: int = 0,
+          agg: str = "all", alpha: float = 1.0, beta: float = 0.0, out: torch.Tensor | None = None,
+          scale: float | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Mean text->visual attention of one layer.  q_text [T][Hq][D], k [Hkv][n_ctx][D] (bf16)."""
+    _dev(q_text, k, out, ws)
+    _bf16(q_text, k)
+    T, Hq, D = q_text.shape
+    Hkv, n_ctx, Dk = k.shape
+    if Dk != D:
+        raise ValueError("head dims differ")
+    rows = {"qhead": Hq, "kvhead": Hkv, "all": 1}[agg]
+    if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing out")
+        out = torch.empty(rows, n_vis, dtype=torch.float32, device=q_text.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (rows, n_vis):
+        raise ValueError("out must be contiguous fp32 [rows][n_vis]")
+    need = score_workspace_bytes(T, Hq, Hkv, q_pos0, n_vis)
+    if ws is None:
+        ws = _ws(need, q_text.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L.call("svlm_score", q_text.data_ptr(), q_text.stride(0), q_text.stride(1), k.data_ptr(), k.stride(0),
+           k.stride(1), L.SVLM_BF16, T, n_ctx, q_pos0, vis_start, n_vis, Hq, Hkv, D, float(scale), _AGG[agg],
+           float(alpha), float(beta), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    return out
+
+
+# ---------------------------------------------------------------------------
+def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: int, with_tag: bool = False):
+    """Two-stage selection per row.  scores [R][F*H*W] fp32 -> (kept [R][budget] int32, n_stage1 [R], tag)."""
+    _dev(scores)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be fp32 [R][n_vis] with contiguous rows")
+    R, n = scores.shape
+    dev = scores.device
+    kept = torch.empty(R, budget, dtype=torch.int32, device=dev)
+    n1 = torch.empty(R, dtype=torch.int32, device=dev)
+    tag = torch.empty(R, n, dtype=torch.uint8, device=dev) if with_tag else None
+    row_stride = scores.stride(0) if R > 1 else n
+    L.call("svlm_select", scores.data_ptr(), row_stride, R, F, H, W, float(top_p), budget,
+           kept.data_ptr(), n1.data_ptr(), tag.data_ptr() if tag is not None else None, None, 0, _stream())
+    return kept, n1, tag
+
+
+# ---------------------------------------------------------------------------
+def gather_kv(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, tail_start: int = 0, n_tail: int = 0,
+              k_dst: torch.Tensor | None = None, v_dst: torch.Tensor | None = None):
+    """k, v [Hkv][N][D] bf16; idx [n_idx] or [Hkv][n_idx] int32 -> compact [Hkv][n_idx+n_tail][D]."""
+    _dev(k, v, idx, k_dst, v_dst)
+    _bf16(k, v)
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if idx.dtype != torch.int32 or idx.stride(-1) != 1:
+        raise ValueError("idx must be int32 with a contiguous last axis")
+    Hkv, N, D = k.shape
+    n_idx = idx.shape[-1]
+    idx_sh = 0 if idx.dim() == 1 else idx.stride(0)
+    n_out = n_idx + n_tail
+    if k_dst is None:
+        k_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
+        v_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
+    if k_dst.stride() != v_dst.stride():
+        raise ValueError("k_dst and v_dst must have the same strides")
+    L.call("svlm_gather_kv", k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1), N, idx.data_ptr(), idx_sh,
+           n_idx, tail_start, n_tail, k_dst.data_ptr(), v_dst.data_ptr(), k_dst.stride(0), k_dst.stride(1), Hkv, D,
+           L.SVLM_BF16, _stream())
+    return k_dst, v_dst
+
+
+# ---------------------------------------------------------------------------
+def decode_attn_workspace_bytes(batch, nq, Hq, Hkv, D, max_kv_len, num_splits=0) -> int:
+    return int(L.load().svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits))
+
+
+def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor, causal_tail: bool,
+                scale: float | None = None, num_splits: int = 0, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None, ws: torch.Tensor | None = None, want_lse: bool = True):
+    """q [B][nq][Hq][D]; k, v [B][Hkv][N][D] or [Hkv][N][D]; kv_len int32 [B] -> (out fp32, lse fp32)."""
+    _dev(q, k, v, kv_len, out, lse, ws)
+    _bf16(q, k, v)
+    B, nq, Hq, D = q.shape
+    if q[0].stride() != (Hq * D, D, 1):
+        raise ValueError("q must be contiguous inside each batch entry")
+    if k.dim() == 3:
+        if B != 1:
+            raise ValueError("3-D KV means batch 1")
+        kv_sb = 0
+        Hkv, N, _ = k.shape
+        kv_sh, kv_sn = k.stride(0), k.stride(1)
+    else:
+        Hkv, N = k.shape[1], k.shape[2]
+        kv_sb, kv_sh, kv_sn = k.stride(0) if B > 1 else 0, k.stride(1), k.stride(2)
+    q_sb = q.stride(0) if B > 1 else nq * Hq * D
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must have identical shapes and strides")
+    if kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("kv_len must be int32 [B]")
+    if out is None:
+        out = torch.empty(B, nq, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
+    need = decode_attn_workspace_bytes(B, nq, Hq, Hkv, D, N, num_splits)
+    if ws is None and need > 0:
+        ws = _ws(need, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L.call("svlm_decode_attn", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn,
+           kv_len.data_ptr(), N, L.SVLM_BF16, B, nq, Hq, Hkv, D, float(scale), 1 if causal_tail else 0,
+           out.data_ptr(), lse.data_ptr() if lse is not None else None, num_splits,
+           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream())
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+def verify_workspace_bytes(batch, gamma, V) -> int:
+    return int(L.load().svlm_verify_workspace(batch, gamma, V))
+
+
+def verify(mode: str, draft_tok: torch.Tensor, target: torch.Tensor, draft_prob: torch.Tensor | None = None,
+           u: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """mode "greedy": target = logits [B][gamma+1][V]; "reject": target = p, draft_prob = q, u [B][gamma+1]."""
+    _dev(draft_tok, target, draft_prob, u, ws)
+    B, gamma = draft_tok.shape
+    V = target.shape[-1]
+    if draft_tok.dtype != torch.int32 or not draft_tok.is_contiguous():
+        raise ValueError("draft_tok must be contiguous int32 [B][gamma]")
+    if target.dtype != torch.float32 or not target.is_contiguous() or tuple(target.shape) != (B, gamma + 1, V):
+        raise ValueError("target must be contiguous fp32 [B][gamma+1][V]")
+    m = {"greedy": L.SVLM_VERIFY_GREEDY, "reject": L.SVLM_VERIFY_REJECT}[mode]
+    if m == L.SVLM_VERIFY_REJECT:
+        if draft_prob is None or u is None:
+            raise ValueError("rejection mode needs draft_prob and u")
+        if tuple(draft_prob.shape) != (B, gamma, V) or not draft_prob.is_contiguous() or draft_prob.dtype != torch.float32:
+            raise ValueError("draft_prob must be contiguous fp32 [B][gamma][V]")
+        if tuple(u.shape) != (B, gamma + 1) or not u.is_contiguous() or u.dtype != torch.float32:
+            raise ValueError("u must be contiguous fp32 [B][gamma+1]")
+    n_acc = torch.empty(B, dtype=torch.int32, device=target.device)
+    nxt = torch.empty(B, dtype=torch.int32, device=target.device)
+    need = verify_workspace_bytes(B, gamma, V)
+    if ws is None:
+        ws = _ws(need, target.device)
+    L.call("svlm_verify", m, B, gamma, V, draft_tok.data_ptr(), target.data_ptr(),
+           draft_prob.data_ptr() if draft_prob is not None else None, u.data_ptr() if u is not None else None,
+           n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    return n_acc, nxt

@@ -13,7 +13,10 @@ allocated so no layer is served from the 256 MB Infinity Cache.
 
 `value` is the decode-attention HBM throughput: algorithmic bytes (every
 needed K and V row read once) of dense verify + 10% draft over the 80 layers,
-divided by their summed kernel time (HIP events on the launch stream).
+divided by their summed launch time.  Each kernel sequence (e.g. the 80
+dense-verify launches of one step) is captured once as a HIP graph and timed
+by HIP events around its replays on the launch stream, so host-side launch
+overhead is excluded and each figure is a per-launch average.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -45,35 +48,6 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     return ap.parse_args()
-
-
-class Timer:
-    """Per-kind kernel timing with events on torch's current stream (the launch stream)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pending = []
-        self.total = {}
-        self.count = {}
-
-    def run(self, kind, fn):
-        t = self.torch
-        a = t.cuda.Event(enable_timing=True)
-        b = t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pending.append((kind, a, b))
-
-    def collect(self):
-        self.torch.cuda.synchronize()
-        for kind, a, b in self.pending:
-            self.total[kind] = self.total.get(kind, 0.0) + a.elapsed_time(b) * 1e3   # us
-            self.count[kind] = self.count.get(kind, 0) + 1
-        self.pending.clear()
-
-    def avg_us(self, kind):
-        return self.total[kind] / self.count[kind]
 
 
 def main():
@@ -148,27 +122,41 @@ def main():
     def k_accept():
         ops.verify("reject", d_t, p_t, q_t, u_t, ws=ws_acc)
 
-    def step(timer=None):
-        run = (lambda kind, fn: timer.run(kind, fn)) if timer else (lambda kind, fn: fn())
-        for l in range(L):
-            run("score", lambda l=l: k_score(l))
-        run("select", k_select)
-        for l in range(L):
-            run("gather", lambda l=l: k_gather(l))
-        for l in range(L):
-            run("draft_attn", lambda l=l: k_draft(l))
-        for l in range(L):
-            run("verify_attn", lambda l=l: k_verify_attn(l))
-        run("accept", k_accept)
+    seqs = {
+        "score": lambda: [k_score(l) for l in range(L)],
+        "select": k_select,
+        "gather": lambda: [k_gather(l) for l in range(L)],
+        "draft_attn": lambda: [k_draft(l) for l in range(L)],
+        "verify_attn": lambda: [k_verify_attn(l) for l in range(L)],
+        "accept": k_accept,
+    }
+    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "verify_attn": L, "accept": 1}
+
+    # warm up eagerly (also fills the library's device-property cache), then capture
+    # each kernel sequence as a HIP graph so host launch overhead is out of the timings
+    for _ in range(max(1, args.warmup)):
+        for fn in seqs.values():
+            fn()
+    torch.cuda.synchronize()
+    graphs = {}
+    for kind, fn in seqs.items():
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        graphs[kind] = gr
+    torch.cuda.synchronize()
+
+    def step():
+        for kind in seqs:
+            graphs[kind].replay()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # (1) whole-step wall time on the stream
+    # (1) whole-step time on the stream
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
         step()
@@ -176,34 +164,39 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # (2) per-kernel durations (events around every call on the launch stream)
-    timer = Timer(torch)
-    for _ in range(args.steps):
-        step(timer)
-        timer.collect()
+    # (2) per-kind launch durations: events around each graph replay, on the launch stream
+    per_us = {}
+    for kind in seqs:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            graphs[kind].replay()
+        b.record()
+        torch.cuda.synchronize()
+        per_us[kind] = a.elapsed_time(b) * 1e3 / (args.steps * calls[kind])
 
     bytes_row = Hkv * D * 2 * 2                       # K + V bytes per key
     verify_bytes = N_full * bytes_row                 # per layer
     draft_bytes = N_draft * bytes_row
-    us_verify = timer.avg_us("verify_attn")
-    us_draft = timer.avg_us("draft_attn")
+    us_verify = per_us["verify_attn"]
+    us_draft = per_us["draft_attn"]
     decode_us_step = L * (us_verify + us_draft)
     decode_gbs = L * (verify_bytes + draft_bytes) / (decode_us_step * 1e-6) / 1e9
     verify_gbs = verify_bytes / (us_verify * 1e-6) / 1e9
     draft_gbs = draft_bytes / (us_draft * 1e-6) / 1e9
-    us_score = timer.avg_us("score")
+    us_score = per_us["score"]
     # pass 1 over every visible (text row, key) pair + pass 2 over (text row, visual key), 2*D flop each
     score_flop = 2 * D * Hq * (T * NV + T * (T + 1) // 2) + 2 * D * Hq * T * NV
 
     kernels = {
-        k: {"us_avg": round(timer.avg_us(k), 3), "calls_per_step": timer.count[k] // args.steps}
-        for k in ("score", "select", "gather", "draft_attn", "verify_attn", "accept")
+        k: {"us_avg": round(per_us[k], 3), "calls_per_step": calls[k]} for k in seqs
     }
     kernels["verify_attn"].update(bytes=verify_bytes, gbs=round(verify_gbs, 1))
     kernels["draft_attn"].update(bytes=draft_bytes, gbs=round(draft_gbs, 1))
     kernels["score"].update(flop=score_flop, tflops=round(score_flop / (us_score * 1e-6) / 1e12, 1))
     kernels["gather"].update(bytes=2 * 2 * (B_keep + T) * Hkv * D * 2,
-                             gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (timer.avg_us("gather") * 1e-6) / 1e9, 1))
+                             gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (per_us["gather"] * 1e-6) / 1e9, 1))
 
     result = {
         "metric": METRIC,

@@ -52,6 +52,12 @@ constexpr int kTile = 32;      // keys per wave step
 constexpr int kMaxRB64 = 5;    // up to 80 query rows per workgroup at D = 64
 constexpr int kMaxRB128 = 3;   // 48 rows at D = 128 (more would spill registers)
 constexpr float kNegInf = -INFINITY;
+constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is raised
+
+// buffer descriptor word 3 for gfx9-family raw buffer loads (no swizzle, no stride)
+constexpr int kBufferFlags = 0x00020000;
+// cache policy of the streaming KV loads: nontemporal
+constexpr int kNT = 2;
 
 template <int DV>
 struct VRaw;
@@ -60,12 +66,25 @@ struct VRaw<8> { typedef unsigned __attribute__((ext_vector_type(4))) T; };
 template <>
 struct VRaw<4> { typedef unsigned __attribute__((ext_vector_type(2))) T; };
 
-template <int D, int RB, int NW>
+template <int DV>
+__device__ __forceinline__ typename VRaw<DV>::T load_v(__amdgpu_buffer_rsrc_t rs, int off);
+template <>
+__device__ __forceinline__ VRaw<8>::T load_v<8>(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
+}
+template <>
+__device__ __forceinline__ VRaw<4>::T load_v<4>(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNT);
+}
+
+template <int D, int RB, int NW, int NB>
 __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   constexpr int KK = D / 32;  // 32-wide d chunks of the QK product
   constexpr int DV = D / 16;  // d values per lane in the PV product
   constexpr int RP = RB * 16;
-  constexpr int LDS_STRIDE = D + 4;
+  constexpr int QSTRIDE = D + 8;       // bf16 elements per staged query row (16-byte pad)
+  constexpr int OSTRIDE = D + 4;       // fp32 elements per merge-slice row
+  constexpr int NSLICE = (NW >= 8) ? 4 : (NW >= 4 ? 2 : 1);
   typedef typename VRaw<DV>::T vraw_t;
 
   const int lane = threadIdx.x & 63;
@@ -84,59 +103,90 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   const int k_begin = s * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, n_kv);
 
-  // ---- query operands (B of the S^T product) and per-row key limits
-  bf16x8 qop[RB][KK];
-  int lim[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = row_base + rb * 16 + c;
-    if (r < a.rows) {
-      const int i = r / a.G;
-      const int hl = r - i * a.G;
-      const uint16_t* qr = a.q + (int64_t)b * a.q_sb + ((int64_t)i * a.Hq + (int64_t)h * a.G + hl) * D;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qop[rb][kk] = as_bf16x8(*(const u32x4*)(qr + kk * 32 + g4 * 8));
-      lim[rb] = min(k_end, a.causal ? n_kv - a.nq + i + 1 : n_kv);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qop[rb][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      lim[rb] = k_end;
-    }
-  }
-
-  float m_run[RB], l_run[RB];
-  f32x4 o[DV][RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < DV; ++mb) o[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const uint16_t* kb = a.k + (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh;
-  const uint16_t* vb = a.v + (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh;
+  // Range-checked buffer descriptors over exactly this split's keys: loads past
+  // k_end return zeros without touching memory, so every load in the stream
+  // is unconditional and the wait counts stay exact.
+  const int64_t row_bytes = a.kv_sn * 2;
+  const int n_rows = max(k_end - k_begin, 0);
+  const int64_t off0 = (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh + (int64_t)k_begin * a.kv_sn;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
 
   struct Tile {
     u32x4 k[2][KK];
     vraw_t v[8];
   };
-
+  // K operand: lane holds K[t0 + 16 kt + c][32 kk + 8 g4 .. +8]; V: the 8 keys
+  // {4g4 .. 4g4+3, 16+4g4 .. 16+4g4+3} of the tile at d = DV*c .. DV*c + DV - 1.
+  // Streaming KV is read once: nontemporal loads.
   auto load_tile = [&](Tile& t, int t0) {
+    const int r0 = t0 - k_begin;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int key = min(t0 + 16 * kt + c, k_end - 1);
-      const uint16_t* kr = kb + (int64_t)key * a.kv_sn + g4 * 8;
+      const int off = (r0 + 16 * kt + c) * (int)row_bytes + g4 * 16;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) t.k[kt][kk] = *(const u32x4*)(kr + kk * 32);
+      for (int kk = 0; kk < KK; ++kk) t.k[kt][kk] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + kk * 64, 0, kNT);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int off = (j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4);
-      const int key = min(t0 + off, k_end - 1);
-      t.v[j] = *(const vraw_t*)(vb + (int64_t)key * a.kv_sn + DV * c);
+      const int row = r0 + ((j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4));
+      t.v[j] = load_v<DV>(vrs, row * (int)row_bytes + DV * 2 * c);
     }
   };
+
+  // this wave's tiles: t = t_first + j * step, j < n_my
+  const int step = kTile * NW;
+  const int t_first = k_begin + kTile * wave;
+  const int n_my = (t_first < k_end) ? (k_end - t_first + step - 1) / step : 0;
+  Tile buf[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) load_tile(buf[i], t_first + i * step);  // first requests go out before anything else
+
+  // ---- stage the query rows of this workgroup in LDS (B operand of S^T = K Q^T)
+  __shared__ __align__(16) unsigned char smem[(size_t)RP * QSTRIDE * 2 > (size_t)NSLICE * RP * OSTRIDE * 4
+                                                    ? (size_t)RP * QSTRIDE * 2
+                                                    : (size_t)NSLICE * RP * OSTRIDE * 4];
+  __shared__ float sm_m[NW][RP];
+  __shared__ float sm_l[NW][RP];
+  uint16_t* sq = (uint16_t*)smem;
+  for (int e = threadIdx.x; e < RP * (D / 8); e += 64 * NW) {
+    const int rr = e / (D / 8), ch = e - rr * (D / 8);
+    const int r = row_base + rr;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r < a.rows) {
+      const int i = r / a.G;
+      const int hl = r - i * a.G;
+      val = *(const u32x4*)(a.q + (int64_t)b * a.q_sb + ((int64_t)i * a.Hq + (int64_t)h * a.G + hl) * D + ch * 8);
+    }
+    *(u32x4*)(sq + rr * QSTRIDE + ch * 8) = val;
+  }
+  int lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row_base + rb * 16 + c;
+    const int i = r / a.G;
+    lim[rb] = (r < a.rows) ? min(k_end, a.causal ? n_kv - a.nq + i + 1 : n_kv) : k_end;
+  }
+  __syncthreads();
+
+  // keys every row of this workgroup may see: tiles below this need no mask
+  const int lim_all = min(k_end, a.causal ? n_kv - a.nq + 1 : n_kv);
+
+  // Running state per row (lane row c + 16 rb, uniform over the four lane
+  // groups): m_use is the reference maximum in log2 units, raised only when a
+  // tile's maximum exceeds it by more than kRescale, so the weights stay
+  // <= 2^kRescale and the fp32 accumulators are rescaled only rarely.
+  float m_use[RB], l_run[RB];
+  f32x4 o[DV][RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_use[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < DV; ++mb) o[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute_tile = [&](const Tile& t, int t0) {
     // S^T blocks: lane holds keys t0 + 16kt + 4g4 + ii for its row
@@ -144,44 +194,43 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) sacc[kt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) acc = mfma16(as_bf16x8(t.k[kt][kk]), qop[rb][kk], acc);
-        sacc[kt][rb] = acc;
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8 qv = as_bf16x8(*(const u32x4*)(sq + (rb * 16 + c) * QSTRIDE + kk * 32 + g4 * 8));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt][rb] = mfma16(as_bf16x8(t.k[kt][kk]), qv, sacc[kt][rb]);
       }
 
+    const bool full = (t0 + kTile <= lim_all);  // wave-uniform
     bf16x8 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float x[8];
-      float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kt = e >> 2, ii = e & 3;
-        const int key = t0 + 16 * kt + 4 * g4 + ii;
-        const float val = sacc[kt][rb][ii] * a.c;
-        x[e] = (key < lim[rb]) ? val : kNegInf;
-        mx = fmaxf(mx, x[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rb] - m_use);
-      m_run[rb] = m_new;
-      float p[8];
-      float ps = 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = sacc[e >> 2][rb][e & 3];
+      if (!full) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(x[e] - m_use);
-        ps += p[e];
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 16 * (e >> 2) + 4 * g4 + (e & 3) >= lim[rb]) x[e] = kNegInf;
       }
-      l_run[rb] = l_run[rb] * alpha + ps;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = max_xor32(max_xor16(mx)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
+      if (__builtin_amdgcn_ballot_w64(mx > m_use[rb] + kRescale) != 0) {
+        const float m_new = fmaxf(m_use[rb], mx);
+        const float alpha = (m_use[rb] == kNegInf) ? 0.f : fast_exp2(m_use[rb] - m_new);
+        l_run[rb] *= alpha;
 #pragma unroll
         for (int mb = 0; mb < DV; ++mb) o[mb][rb] *= alpha;
+        m_use[rb] = m_new;
       }
+      const float mneg = (m_use[rb] == kNegInf) ? 0.f : -m_use[rb];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
+      l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       u32x4 hi, lo;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
@@ -212,37 +261,32 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
     }
   };
 
-  // ---- stream this wave's tiles: t = k_begin + 32 * (wave + NW * j), double buffered
+  // ---- steady state: unconditional loads keep NB tiles in flight; then the tail
   {
-    Tile ta, tb;
-    const int step = kTile * NW;
-    int t = k_begin + kTile * wave;
-    if (t < k_end) load_tile(ta, t);
-    while (t < k_end) {
-      int tn = t + step;
-      if (tn < k_end) load_tile(tb, tn);
-      compute_tile(ta, t);
-      t = tn;
-      if (t >= k_end) break;
-      tn = t + step;
-      if (tn < k_end) load_tile(ta, tn);
-      compute_tile(tb, t);
-      t = tn;
+    int j = 0;
+    for (; j + NB <= n_my; j += NB) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int t = t_first + (j + i) * step;
+        compute_tile(buf[i], t);
+        load_tile(buf[i], t + NB * step);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (j + i < n_my) compute_tile(buf[i], t_first + (j + i) * step);
   }
 
-  // row sums: add the four lane groups (maxima are already uniform across them)
+  // row sums: add the four lane groups (the reference maxima are uniform across them)
+  float m_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] += __shfl_xor(l_run[rb], 16);
-    l_run[rb] += __shfl_xor(l_run[rb], 32);
+    l_run[rb] = sum_xor32(sum_xor16(l_run[rb]));
+    m_run[rb] = m_use[rb];
   }
 
-  // ---- merge the waves of the workgroup (fixed order)
+  // ---- merge the waves of the workgroup in a fixed tree order
   if constexpr (NW > 1) {
-    __shared__ float sm_m[NW][RP];
-    __shared__ float sm_l[NW][RP];
-    __shared__ float sm_o[(NW >= 4) ? 2 : 1][RP * LDS_STRIDE];
     if (g4 == 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -250,7 +294,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
         sm_l[wave][rb * 16 + c] = l_run[rb];
       }
     }
-    __syncthreads();
+    __syncthreads();  // also ends every use of the staged queries: smem is reused below
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = rb * 16 + c;
@@ -269,14 +313,17 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
       m_run[rb] = M;
       l_run[rb] = L;
     }
+    float* slices = (float*)smem;
+    auto slice = [&](int k) { return slices + (size_t)k * RP * OSTRIDE; };
     auto store_slice = [&](float* sl) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int mb = 0; mb < DV; ++mb)
-            sl[(rb * 16 + c) * LDS_STRIDE + DV * (4 * g4 + i) + mb] = o[mb][rb][i];
+          for (int mb = 0; mb < DV; mb += 4)
+            *(float4*)(sl + (rb * 16 + c) * OSTRIDE + DV * (4 * g4 + i) + mb) =
+                make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
     };
     auto add_slice = [&](const float* sl) {
 #pragma unroll
@@ -284,26 +331,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int mb = 0; mb < DV; ++mb)
-            o[mb][rb][i] += sl[(rb * 16 + c) * LDS_STRIDE + DV * (4 * g4 + i) + mb];
+          for (int mb = 0; mb < DV; mb += 4) {
+            const float4 v = *(const float4*)(sl + (rb * 16 + c) * OSTRIDE + DV * (4 * g4 + i) + mb);
+            o[mb][rb][i] += v.x;
+            o[mb + 1][rb][i] += v.y;
+            o[mb + 2][rb][i] += v.z;
+            o[mb + 3][rb][i] += v.w;
+          }
     };
-    if constexpr (NW >= 4) {
-      // ((w0 + w2) + (w1 + w3))
-      if (wave >= 2) store_slice(sm_o[wave - 2]);
+    // rounds: waves [half, width) hand their sums to waves [0, half)
+#pragma unroll
+    for (int width = NW; width > 1; width >>= 1) {
+      const int half = width >> 1;
+      if (wave >= half && wave < width) store_slice(slice(wave - half));
       __syncthreads();
-      if (wave < 2) {
-        add_slice(sm_o[wave]);
-        if (wave == 1) store_slice(sm_o[1]);
-      }
+      if (wave < half) add_slice(slice(wave));
       __syncthreads();
-      if (wave != 0) return;
-      add_slice(sm_o[1]);
-    } else {
-      if (wave == 1) store_slice(sm_o[0]);
-      __syncthreads();
-      if (wave != 0) return;
-      add_slice(sm_o[0]);
     }
+    if (wave != 0) return;
   }
 
   // ---- write: final output (one split) or the partial state of this split
@@ -343,37 +388,64 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one query row in split order.
+// Merge the split partials of one query row per wave, in split order.  Every
+// partial load of a row is independent, so they are all in flight at once.
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine(AttnArgs a) {
-  const int64_t R = blockIdx.x;
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int64_t rows_total) {
+  constexpr int PL = D / 64;  // output columns per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (R >= rows_total) return;
+  const float* ml = a.ws_ml + R * a.splits * 2;
+  const float* po = a.ws_o + R * a.splits * D + lane * PL;
+  float M = kNegInf;
+  for (int s0 = lane; s0 < a.splits; s0 += 64) M = fmaxf(M, ml[2 * s0]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float L = 0.f;
+  float acc[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 16
+    for (int s = 0; s < a.splits; ++s) {
+      const float2 st = *(const float2*)(ml + 2 * s);
+      const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
+      L += st.y * w;
+      if constexpr (PL == 2) {
+        const float2 v = *(const float2*)(po + (int64_t)s * D);
+        acc[0] += w * v.x;
+        acc[1] += w * v.y;
+      } else {
+        acc[0] += w * po[(int64_t)s * D];
+      }
+    }
+  }
   const int r = (int)(R % a.rows);
   const int64_t bh = R / a.rows;
   const int h = (int)(bh % a.Hkv);
   const int b = (int)(bh / a.Hkv);
-  const int d = threadIdx.x;
-  const float* ml = a.ws_ml + R * a.splits * 2;
-  const float* po = a.ws_o + R * a.splits * D + d;
-  float M = kNegInf;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float acc = 0.f, L = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = ml[2 * s];
-    const float w = (ms == kNegInf) ? 0.f : exp2f(ms - M);
-    L += ml[2 * s + 1] * w;
-    acc += w * po[(int64_t)s * D];
-  }
   const int i = r / a.G;
   const int hl = r - i * a.G;
   const int64_t orow = ((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl;
-  a.out[orow * D + d] = (L > 0.f) ? acc / L : 0.f;
-  if (a.lse && d == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) a.out[orow * D + lane * PL + e] = acc[e] * inv;
+  if (a.lse && lane == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+// tiles in flight per wave: eight-wave workgroups run two waves per SIMD, which
+// hide each other's memory latency, so one tile per wave fits their register
+// budget; narrower workgroups keep two.
+template <int D, int RB, int NW>
+constexpr int pipeline_depth() {
+  return (NW >= 8) ? 1 : 2;
 }
 
 template <int D, int RB, int NW>
 void launch_rb(const AttnArgs& a, int batch, int row_chunks, hipStream_t st) {
   dim3 grid((unsigned)(batch * a.Hkv * a.splits), (unsigned)row_chunks);
-  attn_splitk<D, RB, NW><<<grid, 64 * NW, 0, st>>>(a);
+  attn_splitk<D, RB, NW, pipeline_depth<D, RB, NW>()><<<grid, 64 * NW, 0, st>>>(a);
 }
 
 template <int D, int NW>
@@ -393,7 +465,8 @@ void launch_nw(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t
 
 template <int D>
 void launch_d(const AttnArgs& a, int nw, int rb, int batch, int row_chunks, hipStream_t st) {
-  if (nw == 4) launch_nw<D, 4>(a, rb, batch, row_chunks, st);
+  if (nw == 8) launch_nw<D, 8>(a, rb, batch, row_chunks, st);
+  else if (nw == 4) launch_nw<D, 4>(a, rb, batch, row_chunks, st);
   else if (nw == 2) launch_nw<D, 2>(a, rb, batch, row_chunks, st);
   else launch_nw<D, 1>(a, rb, batch, row_chunks, st);
 }
@@ -419,7 +492,7 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
   const int tiles_per_split = (tiles + splits - 1) / splits;
   p.keys_per_split = tiles_per_split * kTile;
   p.splits = (max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
-  p.nw = tiles_per_split >= 4 ? 4 : (tiles_per_split >= 2 ? 2 : 1);
+  p.nw = tiles_per_split >= 8 ? 8 : (tiles_per_split >= 4 ? 4 : (tiles_per_split >= 2 ? 2 : 1));
   return p;
 }
 
@@ -491,8 +564,9 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   if (D == 128) launch_d<128>(a, p.nw, p.rb, batch, p.row_chunks, st);
   else launch_d<64>(a, p.nw, p.rb, batch, p.row_chunks, st);
   if (p.splits > 1) {
-    if (D == 128) attn_combine<128><<<(unsigned)rows_total, 128, 0, st>>>(a);
-    else attn_combine<64><<<(unsigned)rows_total, 64, 0, st>>>(a);
+    const unsigned blocks = (unsigned)((rows_total + 3) / 4);
+    if (D == 128) attn_combine<128><<<blocks, 256, 0, st>>>(a, (int64_t)rows_total);
+    else attn_combine<64><<<blocks, 256, 0, st>>>(a, (int64_t)rows_total);
   }
   return check_launch("svlm_decode_attn");
 }

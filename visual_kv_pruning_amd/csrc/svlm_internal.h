@@ -49,6 +49,25 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 
+// Cross-lane butterflies on the VALU (gfx950 v_permlane16/32_swap): after the
+// swap the two results hold the values of lanes l and l ^ 16 (or l ^ 32).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  return fmaxf(bits_f(r[0]), bits_f(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return fmaxf(bits_f(r[0]), bits_f(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  return bits_f(r[0]) + bits_f(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return bits_f(r[0]) + bits_f(r[1]);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

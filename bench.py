@@ -95,8 +95,8 @@ def main():
 
     row = torch.empty(1, NV, dtype=torch.float32, device=dev)
     ws_score = torch.empty(ops.score_workspace_bytes(T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
-    ws_v = torch.empty(max(16, ops.decode_attn_workspace_bytes(1, nqv, Hq, Hkv, D, N_full)), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(max(16, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, nqv, Hq, Hkv, D, N_full)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)), dtype=torch.uint8, device=dev)
     ws_acc = torch.empty(ops.verify_workspace_bytes(1, gv, V), dtype=torch.uint8, device=dev)
     o_v = torch.empty(1, nqv, Hq, D, dtype=torch.float32, device=dev)
     l_v = torch.empty(1, nqv, Hq, dtype=torch.float32, device=dev)

@@ -178,7 +178,8 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
  *   chip.  With more than one split the partial (max, sum, output) states go
  *   to ws and are merged in a fixed order.
  * ws: svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits)
- *   bytes (0 when one split suffices).
+ *   bytes (0 when one split suffices); no initial contents are needed.  Two
+ *   calls that overlap in time must not share a workspace.
  * Works in bf16 matrix-core products with fp32 accumulation; the softmax
  * weights enter the value product as a bf16 hi + lo pair, so the output
  * keeps fp32-level accuracy.

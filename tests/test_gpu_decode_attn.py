@@ -83,6 +83,33 @@ def test_forced_split_counts_agree(splits):
     _check(q, k, v, [3000], True, num_splits=splits, name=f"splits={splits}")
 
 
+@pytest.mark.parametrize("nq,splits", [(1, 14), (6, 3), (6, 40)])
+def test_workspace_reused_across_calls(nq, splits):
+    """One workspace serves repeated calls; results are identical each time."""
+    from visual_kv_pruning_amd import ops
+    q = _rand(41, 1, nq, 16, 128)
+    k = _rand(42, 2, 3000, 128)
+    v = _rand(43, 2, 3000, 128)
+    ro, rl = oracle.decode_attn(q, k, v, [3000], nq > 1)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    kl = torch.tensor([3000], dtype=torch.int32, device="cuda:0")
+    need = ops.decode_attn_workspace_bytes(1, nq, 16, 2, 128, 3000, splits)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    log(f"decode_attn case workspace reuse nq={nq} splits={splits} ws={need}")
+    first = None
+    for rep in range(3):
+        out = torch.full((1, nq, 16, 128), float("nan"), device="cuda:0")
+        lse = torch.full((1, nq, 16), float("nan"), device="cuda:0")
+        ops.decode_attn(qd, kd, vd, kl, nq > 1, num_splits=splits, out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        assert row_rel_err(o, ro) <= TOL and np.abs(l - rl).max() <= 1e-3, rep
+        if first is None:
+            first = (o, l)
+        else:
+            assert np.array_equal(first[0], o) and np.array_equal(first[1], l), rep
+
+
 def test_batch_with_ragged_lengths_and_strided_cache():
     B, nq, Hq, Hkv, D, Ncap = 3, 4, 8, 2, 128, 700
     q = _rand(11, B, nq, Hq, D)

@@ -38,7 +38,7 @@ struct AttnArgs {
   int64_t kv_sb, kv_sh, kv_sn;
   const int32_t* kv_len;
   int max_kv_len;
-  int nq, Hq, Hkv, G, rows;
+  int batch, nq, Hq, Hkv, G, rows;
   float c;  // scale * log2(e)
   int causal;
   int splits, keys_per_split;
@@ -66,6 +66,20 @@ struct VRaw<8> { typedef unsigned __attribute__((ext_vector_type(4))) T; };
 template <>
 struct VRaw<4> { typedef unsigned __attribute__((ext_vector_type(2))) T; };
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int enc = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+  __builtin_amdgcn_s_waitcnt(enc);
+  __asm__ volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __asm__ volatile("" ::: "memory");
+}
+
 template <int DV>
 __device__ __forceinline__ typename VRaw<DV>::T load_v(__amdgpu_buffer_rsrc_t rs, int off);
 template <>
@@ -77,14 +91,36 @@ __device__ __forceinline__ VRaw<4>::T load_v<4>(__amdgpu_buffer_rsrc_t rs, int o
   return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNT);
 }
 
-template <int D, int RB, int NW, int NB>
-__global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
-  constexpr int KK = D / 32;  // 32-wide d chunks of the QK product
-  constexpr int DV = D / 16;  // d values per lane in the PV product
+// Depth of the per-wave staging ring: as many K/V tiles in flight as the LDS
+// (160 KB per CU, one workgroup per CU) holds, with every outstanding transfer
+// countable by the 6-bit vector-memory wait counter.
+template <int D, int RB, int NW>
+constexpr int ring_depth() {
+  constexpr int TB = kTile * D * 2;
+  constexpr int NI = TB / 1024;
   constexpr int RP = RB * 16;
-  constexpr int QSTRIDE = D + 8;       // bf16 elements per staged query row (16-byte pad)
-  constexpr int OSTRIDE = D + 4;       // fp32 elements per merge-slice row
-  constexpr int NSLICE = (NW >= 8) ? 4 : (NW >= 4 ? 2 : 1);
+  constexpr size_t slice_bytes = (size_t)RP * (D + 4) * 4;
+  int best = 1;
+  for (int ns = 1; ns <= 4; ++ns) {
+    const size_t slot = (size_t)NW * ns * TB;
+    const size_t ks = slot > ((NW + 1) / 2) * slice_bytes ? slot : ((NW + 1) / 2) * slice_bytes;
+    const size_t vs = slot > (NW / 2) * slice_bytes ? slot : (NW / 2) * slice_bytes;
+    const size_t lds = ks + vs + (size_t)RP * D * 2 + 2 * (size_t)NW * RP * 4 + 64;
+    if (2 * ns * NI <= 63 && lds <= 160 * 1024) best = ns;
+  }
+  return best;
+}
+
+template <int D, int RB, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
+  constexpr int KK = D / 32;             // 32-wide d chunks of the QK product
+  constexpr int DV = D / 16;             // d values per lane in the PV product
+  constexpr int RP = RB * 16;
+  constexpr int ROWB = D * 2;            // bytes of one K or V row in a staged tile
+  constexpr int CH = ROWB / 16;          // 16-byte chunks per row
+  constexpr int TB = kTile * ROWB;       // bytes of one staged K (or V) tile
+  constexpr int NI = TB / 1024;          // 1 KB transfers per K (or V) tile
+  constexpr int OSTRIDE = D + 4;         // fp32 elements per merge-slice row
   typedef typename VRaw<DV>::T vraw_t;
 
   const int lane = threadIdx.x & 63;
@@ -103,9 +139,26 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   const int k_begin = s * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, n_kv);
 
-  // Range-checked buffer descriptors over exactly this split's keys: loads past
-  // k_end return zeros without touching memory, so every load in the stream
-  // is unconditional and the wait counts stay exact.
+  // LDS: one K + V staging slot per wave; staged query rows; per-wave row state.
+  // The slot area is reused for the merge slices after the key loop.
+  // K and V slots are distinct objects so the compiler can tell their transfers apart.
+  // NS staging slots per wave form a ring, so NS tiles are in flight per wave.
+  // After the key loop the slots hold the merge slices: the first half of the
+  // slices in kslots, the rest in vslots.
+  constexpr size_t SLOT_BYTES = (size_t)NW * NS * TB;
+  constexpr int NSLICE = NW;
+  constexpr size_t SLICE_BYTES = (size_t)RP * OSTRIDE * 4;
+  constexpr size_t KS_BYTES = SLOT_BYTES > ((NSLICE + 1) / 2) * SLICE_BYTES ? SLOT_BYTES : ((NSLICE + 1) / 2) * SLICE_BYTES;
+  constexpr size_t VS_BYTES = SLOT_BYTES > (NSLICE / 2) * SLICE_BYTES ? SLOT_BYTES : (NSLICE / 2) * SLICE_BYTES;
+  __shared__ __align__(16) unsigned char kslots[KS_BYTES];
+  __shared__ __align__(16) unsigned char vslots[VS_BYTES];
+  __shared__ __align__(16) unsigned char sq[RP * ROWB];  // query rows, chunks swizzled like the KV tiles
+  __shared__ float sm_m[NW][RP];
+  __shared__ float sm_l[NW][RP];
+
+  // Range-checked buffer descriptors over exactly this split's keys: transfers
+  // past k_end deliver zeros without touching memory, so every transfer is
+  // issued unconditionally and the wait counts below are static.
   const int64_t row_bytes = a.kv_sn * 2;
   const int n_rows = max(k_end - k_begin, 0);
   const int64_t off0 = (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh + (int64_t)k_begin * a.kv_sn;
@@ -114,54 +167,58 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
 
-  struct Tile {
-    u32x4 k[2][KK];
-    vraw_t v[8];
-  };
-  // K operand: lane holds K[t0 + 16 kt + c][32 kk + 8 g4 .. +8]; V: the 8 keys
-  // {4g4 .. 4g4+3, 16+4g4 .. 16+4g4+3} of the tile at d = DV*c .. DV*c + DV - 1.
-  // Streaming KV is read once: nontemporal loads.
-  auto load_tile = [&](Tile& t, int t0) {
+  unsigned char* kring = kslots + (size_t)wave * NS * TB;
+  unsigned char* vring = vslots + (size_t)wave * NS * TB;
+
+  // Global -> LDS transfer of 32 rows, row-major with 16-byte chunks XOR-swizzled
+  // by row (chunk p of row r holds source chunk p ^ (r % CH)); every lane moves
+  // 16 bytes and lands at slot + 1 KB * i + 16 * lane.  Nontemporal: read once.
+  auto stage = [&](__amdgpu_buffer_rsrc_t rs, unsigned char* slot, int t0) {
     const int r0 = t0 - k_begin;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int off = (r0 + 16 * kt + c) * (int)row_bytes + g4 * 16;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) t.k[kt][kk] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + kk * 64, 0, kNT);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = r0 + ((j < 4) ? (4 * g4 + j) : (16 + 4 * g4 + j - 4));
-      t.v[j] = load_v<DV>(vrs, row * (int)row_bytes + DV * 2 * c);
+    for (int i = 0; i < NI; ++i) {
+      const int r = i * (1024 / ROWB) + lane / CH;
+      const int p = lane % CH;
+      const int src = (r0 + r) * (int)row_bytes + ((p ^ (r % CH)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(slot + i * 1024), 16,
+                                               src, 0, 0, kNT);
     }
   };
+  // chunk `ch` of staged row r
+  auto chunk_at = [&](const unsigned char* slot, int r, int ch) { return slot + r * ROWB + ((ch ^ (r % CH)) * 16); };
+
+  // ---- stage the query rows of this workgroup (B operand of S^T = K Q^T) by
+  // LDS DMA, first; rows past the last query read as zeros
+  {
+    const int64_t qbytes = (int64_t)a.nq * a.Hq * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.q + (int64_t)b * a.q_sb), (short)0, (int)qbytes, kBufferFlags);
+    constexpr int QI = RP * ROWB / 1024;  // 1 KB transfers for the staged rows
+    for (int i = wave; i < QI; i += NW) {
+      const int rr = i * (1024 / ROWB) + lane / CH;
+      const int p = lane % CH;
+      const int r = row_base + rr;
+      int src = (int)qbytes;  // out of range: zeros
+      if (r < a.rows) {
+        const int qi = r / a.G;
+        const int hl = r - qi * a.G;
+        src = ((qi * a.Hq + h * a.G + hl) * D) * 2 + ((p ^ (rr % CH)) * 16);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(sq + i * 1024), 16, src,
+                                               0, 0, 0);
+    }
+  }
 
   // this wave's tiles: t = t_first + j * step, j < n_my
   const int step = kTile * NW;
   const int t_first = k_begin + kTile * wave;
   const int n_my = (t_first < k_end) ? (k_end - t_first + step - 1) / step : 0;
-  Tile buf[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) load_tile(buf[i], t_first + i * step);  // first requests go out before anything else
-
-  // ---- stage the query rows of this workgroup in LDS (B operand of S^T = K Q^T)
-  __shared__ __align__(16) unsigned char smem[(size_t)RP * QSTRIDE * 2 > (size_t)NSLICE * RP * OSTRIDE * 4
-                                                    ? (size_t)RP * QSTRIDE * 2
-                                                    : (size_t)NSLICE * RP * OSTRIDE * 4];
-  __shared__ float sm_m[NW][RP];
-  __shared__ float sm_l[NW][RP];
-  uint16_t* sq = (uint16_t*)smem;
-  for (int e = threadIdx.x; e < RP * (D / 8); e += 64 * NW) {
-    const int rr = e / (D / 8), ch = e - rr * (D / 8);
-    const int r = row_base + rr;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r < a.rows) {
-      const int i = r / a.G;
-      const int hl = r - i * a.G;
-      val = *(const u32x4*)(a.q + (int64_t)b * a.q_sb + ((int64_t)i * a.Hq + (int64_t)h * a.G + hl) * D + ch * 8);
-    }
-    *(u32x4*)(sq + rr * QSTRIDE + ch * 8) = val;
+  for (int q = 0; q < NS; ++q) {  // unconditional: past k_end these deliver zeros
+    stage(krs, kring + q * TB, t_first + q * step);
+    stage(vrs, vring + q * TB, t_first + q * step);
   }
+  wait_vmcnt<2 * NS * NI>();  // this wave's query transfers have landed
   int lim[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -169,10 +226,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
     const int i = r / a.G;
     lim[rb] = (r < a.rows) ? min(k_end, a.causal ? n_kv - a.nq + i + 1 : n_kv) : k_end;
   }
-  __syncthreads();
-
   // keys every row of this workgroup may see: tiles below this need no mask
   const int lim_all = min(k_end, a.causal ? n_kv - a.nq + 1 : n_kv);
+  __syncthreads();
 
   // Running state per row (lane row c + 16 rb, uniform over the four lane
   // groups): m_use is the reference maximum in log2 units, raised only when a
@@ -188,7 +244,21 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
     for (int mb = 0; mb < DV; ++mb) o[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_tile = [&](const Tile& t, int t0) {
+  for (int j = 0; j < n_my; ++j) {
+    const int t0 = t_first + j * step;
+    unsigned char* kslot = kring + (j % NS) * TB;
+    unsigned char* vslot = vring + (j % NS) * TB;
+    // Issue order is K(t) V(t) K(t+1) V(t+1) ... K(t+NS-1) V(t+NS-1): K(t) has
+    // landed once at most 2 NS - 1 groups of NI transfers are outstanding.
+    wait_vmcnt<(2 * NS - 1) * NI>();
+    u32x4 kt_[2][KK];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kt_[kt][kk] = *(const u32x4*)chunk_at(kslot, 16 * kt + c, kk * 4 + g4);
+    wait_lgkmcnt0();
+    stage(krs, kslot, t0 + NS * step);  // K(t+NS): out of range past the last tile, i.e. zeros
+
     // S^T blocks: lane holds keys t0 + 16kt + 4g4 + ii for its row
     f32x4 sacc[2][RB];
 #pragma unroll
@@ -199,37 +269,57 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bf16x8 qv = as_bf16x8(*(const u32x4*)(sq + (rb * 16 + c) * QSTRIDE + kk * 32 + g4 * 8));
+        const bf16x8 qv = as_bf16x8(*(const u32x4*)chunk_at(sq, rb * 16 + c, kk * 4 + g4));
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc[kt][rb] = mfma16(as_bf16x8(t.k[kt][kk]), qv, sacc[kt][rb]);
+        for (int kt = 0; kt < 2; ++kt) sacc[kt][rb] = mfma16(as_bf16x8(kt_[kt][kk]), qv, sacc[kt][rb]);
       }
 
+    // V(t) has landed once at most 2 NS - 1 groups are outstanding (K(t+NS) included)
+    wait_vmcnt<(2 * NS - 1) * NI>();
+    vraw_t vt[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int r = (jj < 4) ? (4 * g4 + jj) : (16 + 4 * g4 + jj - 4);
+      if constexpr (DV == 8) vt[jj] = *(const vraw_t*)chunk_at(vslot, r, c);
+      else vt[jj] = *(const vraw_t*)(chunk_at(vslot, r, c >> 1) + (c & 1) * 8);
+    }
+    wait_lgkmcnt0();
+    stage(vrs, vslot, t0 + NS * step);
+
     const bool full = (t0 + kTile <= lim_all);  // wave-uniform
-    bf16x8 phi[RB], plo[RB];
+    float x[RB][8], mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = sacc[e >> 2][rb][e & 3];
-      if (!full) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t0 + 16 * (e >> 2) + 4 * g4 + (e & 3) >= lim[rb]) x[e] = kNegInf;
+      for (int e = 0; e < 8; ++e) {
+        const float v = sacc[e >> 2][rb][e & 3];
+        x[rb][e] = (full || t0 + 16 * (e >> 2) + 4 * g4 + (e & 3) < lim[rb]) ? v : kNegInf;
       }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = max_xor32(max_xor16(mx)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
-      if (__builtin_amdgcn_ballot_w64(mx > m_use[rb] + kRescale) != 0) {
-        const float m_new = fmaxf(m_use[rb], mx);
+      float m = fmaxf(fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])),
+                      fmaxf(fmaxf(x[rb][4], x[rb][5]), fmaxf(x[rb][6], x[rb][7])));
+      mx[rb] = max_xor32(max_xor16(m)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
+    }
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) grow |= (mx[rb] > m_use[rb] + kRescale);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m_use[rb], mx[rb]);
         const float alpha = (m_use[rb] == kNegInf) ? 0.f : fast_exp2(m_use[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
         for (int mb = 0; mb < DV; ++mb) o[mb][rb] *= alpha;
         m_use[rb] = m_new;
       }
+    }
+    bf16x8 phi[RB], plo[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       const float mneg = (m_use[rb] == kNegInf) ? 0.f : -m_use[rb];
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[rb][e], a.c, mneg));
       l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       u32x4 hi, lo;
 #pragma unroll
@@ -243,39 +333,31 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
       phi[rb] = as_bf16x8(hi);
       plo[rb] = as_bf16x8(lo);
     }
-
-    // O^T += V^T P^T; lane's A operand for block mb is d = DV*c + mb over its 8 keys
+    // O^T += V^T P^T, two column blocks at a time (hi and lo products into one
+    // accumulator are 2 * RB instructions apart)
 #pragma unroll
-    for (int mb = 0; mb < DV; ++mb) {
-      const int w = mb >> 1;
-      const unsigned sel = (mb & 1) ? kPermHi : kPermLo;
-      u32x4 vv;
+    for (int mb = 0; mb < DV; mb += 2) {
+      bf16x8 vop[2];
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) vv[qd] = perm(t.v[2 * qd + 1][w], t.v[2 * qd][w], sel);
-      const bf16x8 vop = as_bf16x8(vv);
+      for (int u = 0; u < 2; ++u) {
+        const int w = (mb + u) >> 1;
+        const unsigned sel = ((mb + u) & 1) ? kPermHi : kPermLo;
+        u32x4 vv;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        o[mb][rb] = mfma16(vop, phi[rb], o[mb][rb]);
-        o[mb][rb] = mfma16(vop, plo[rb], o[mb][rb]);
+        for (int qd = 0; qd < 4; ++qd) vv[qd] = perm(vt[2 * qd + 1][w], vt[2 * qd][w], sel);
+        vop[u] = as_bf16x8(vv);
       }
-    }
-  };
-
-  // ---- steady state: unconditional loads keep NB tiles in flight; then the tail
-  {
-    int j = 0;
-    for (; j + NB <= n_my; j += NB) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int t = t_first + (j + i) * step;
-        compute_tile(buf[i], t);
-        load_tile(buf[i], t + NB * step);
-      }
-    }
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      if (j + i < n_my) compute_tile(buf[i], t_first + (j + i) * step);
+        for (int rb = 0; rb < RB; ++rb) o[mb + u][rb] = mfma16(vop[u], phi[rb], o[mb + u][rb]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[mb + u][rb] = mfma16(vop[u], plo[rb], o[mb + u][rb]);
+    }
   }
+  wait_vmcnt<0>();  // the zero-filled transfers past the end must land before the slots are reused
 
   // row sums: add the four lane groups (the reference maxima are uniform across them)
   float m_run[RB];
@@ -285,7 +367,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
     m_run[rb] = m_use[rb];
   }
 
-  // ---- merge the waves of the workgroup in a fixed tree order
+  // ---- merge the waves of the workgroup: each wave scales its sums to the
+  // common row maximum and parks them in its own LDS slice; then all threads
+  // add the slices in wave order and write the rows with coalesced stores.
   if constexpr (NW > 1) {
     if (g4 == 0) {
 #pragma unroll
@@ -294,158 +378,175 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
         sm_l[wave][rb * 16 + c] = l_run[rb];
       }
     }
-    __syncthreads();  // also ends every use of the staged queries: smem is reused below
+    __syncthreads();  // every wave is past its key loop: the slot area is reused below
+    auto slice = [&](int k) {
+      constexpr int KH = (NSLICE + 1) / 2;
+      return (k < KH) ? (float*)kslots + (size_t)k * RP * OSTRIDE : (float*)vslots + (size_t)(k - KH) * RP * OSTRIDE;
+    };
+    {
+      float* sl = slice(wave);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = rb * 16 + c;
-      float M = kNegInf;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = rb * 16 + c;
+        float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][row]);
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w][row];
-        L += (mw == kNegInf) ? 0.f : sm_l[w][row] * exp2f(mw - M);
-      }
-      const float f = (m_run[rb] == kNegInf) ? 0.f : exp2f(m_run[rb] - M);
-#pragma unroll
-      for (int mb = 0; mb < DV; ++mb) o[mb][rb] *= f;
-      m_run[rb] = M;
-      l_run[rb] = L;
-    }
-    float* slices = (float*)smem;
-    auto slice = [&](int k) { return slices + (size_t)k * RP * OSTRIDE; };
-    auto store_slice = [&](float* sl) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][row]);
+        const float f = (m_run[rb] == kNegInf) ? 0.f : exp2f(m_run[rb] - M);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int mb = 0; mb < DV; mb += 4)
-            *(float4*)(sl + (rb * 16 + c) * OSTRIDE + DV * (4 * g4 + i) + mb) =
-                make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
-    };
-    auto add_slice = [&](const float* sl) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int mb = 0; mb < DV; mb += 4) {
-            const float4 v = *(const float4*)(sl + (rb * 16 + c) * OSTRIDE + DV * (4 * g4 + i) + mb);
-            o[mb][rb][i] += v.x;
-            o[mb + 1][rb][i] += v.y;
-            o[mb + 2][rb][i] += v.z;
-            o[mb + 3][rb][i] += v.w;
-          }
-    };
-    // rounds: waves [half, width) hand their sums to waves [0, half)
-#pragma unroll
-    for (int width = NW; width > 1; width >>= 1) {
-      const int half = width >> 1;
-      if (wave >= half && wave < width) store_slice(slice(wave - half));
-      __syncthreads();
-      if (wave < half) add_slice(slice(wave));
-      __syncthreads();
+            *(float4*)(sl + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
+                make_float4(o[mb][rb][i] * f, o[mb + 1][rb][i] * f, o[mb + 2][rb][i] * f, o[mb + 3][rb][i] * f);
+      }
     }
-    if (wave != 0) return;
+    __syncthreads();
+    constexpr int C4 = D / 4;
+    for (int e = threadIdx.x; e < RP * C4; e += 64 * NW) {
+      const int row = e / C4, d4 = e - row * C4;
+      const int r = row_base + row;
+      if (r >= a.rows) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][row]);
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][row];
+        L += (mw == kNegInf) ? 0.f : sm_l[w][row] * exp2f(mw - M);
+        const float4 v = *(const float4*)(slice(w) + row * OSTRIDE + 4 * d4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      const int qi = r / a.G;
+      const int hl = r - qi * a.G;
+      if (a.splits == 1) {
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+        const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
+        *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+      } else {
+        const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
+        *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
+        if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
+      }
+    }
+  } else {
+    // ---- one wave: write the final output (one split) or this split's partial state
+  #pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = row_base + rb * 16 + c;
+      if (r >= a.rows) continue;
+      const int i = r / a.G;
+      const int hl = r - i * a.G;
+      if (a.splits == 1) {
+        const float L = l_run[rb];
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+        float* orow = a.out + (((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl) * D;
+  #pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+  #pragma unroll
+          for (int mb = 0; mb < DV; mb += 4) {
+            float4 vv = make_float4(o[mb][rb][i4] * inv, o[mb + 1][rb][i4] * inv, o[mb + 2][rb][i4] * inv,
+                                    o[mb + 3][rb][i4] * inv);
+            *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
+          }
+        if (a.lse && g4 == 0)
+          a.lse[((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl] =
+              (L > 0.f) ? (m_run[rb] + log2f(L)) * kLn2 : kNegInf;
+      } else {
+        const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
+        float* orow = a.ws_o + (R * a.splits + s) * D;
+  #pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+  #pragma unroll
+          for (int mb = 0; mb < DV; mb += 4) {
+            float4 vv = make_float4(o[mb][rb][i4], o[mb + 1][rb][i4], o[mb + 2][rb][i4], o[mb + 3][rb][i4]);
+            *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
+          }
+        if (g4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(m_run[rb], l_run[rb]);
+      }
+    }
   }
 
-  // ---- write: final output (one split) or the partial state of this split
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = row_base + rb * 16 + c;
-    if (r >= a.rows) continue;
-    const int i = r / a.G;
-    const int hl = r - i * a.G;
-    if (a.splits == 1) {
-      const float L = l_run[rb];
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;
-      float* orow = a.out + (((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl) * D;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-#pragma unroll
-        for (int mb = 0; mb < DV; mb += 4) {
-          float4 vv = make_float4(o[mb][rb][i4] * inv, o[mb + 1][rb][i4] * inv, o[mb + 2][rb][i4] * inv,
-                                  o[mb + 3][rb][i4] * inv);
-          *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
-        }
-      if (a.lse && g4 == 0)
-        a.lse[((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl] =
-            (L > 0.f) ? (m_run[rb] + log2f(L)) * kLn2 : kNegInf;
-    } else {
-      const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
-      float* orow = a.ws_o + (R * a.splits + s) * D;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-#pragma unroll
-        for (int mb = 0; mb < DV; mb += 4) {
-          float4 vv = make_float4(o[mb][rb][i4], o[mb + 1][rb][i4], o[mb + 2][rb][i4], o[mb + 3][rb][i4]);
-          *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
-        }
-      if (g4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(m_run[rb], l_run[rb]);
-    }
-  }
 }
 
-// Merge the split partials of one query row per wave, in split order.  Every
-// partial load of a row is independent, so they are all in flight at once.
+// Separate merge launch for large partial volumes: kCombineRows rows per
+// workgroup, 128 threads per row = D/4 column groups x (512/D) split parts.
+// Every thread issues all loads of its splits at once (one memory round trip),
+// merges them against its own running maximum, and the parts are combined in
+// a fixed order through LDS.  Deterministic.
+constexpr int kCombineRows = 2;
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int64_t rows_total) {
-  constexpr int PL = D / 64;  // output columns per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (R >= rows_total) return;
-  const float* ml = a.ws_ml + R * a.splits * 2;
-  const float* po = a.ws_o + R * a.splits * D + lane * PL;
-  float M = kNegInf;
-  for (int s0 = lane; s0 < a.splits; s0 += 64) M = fmaxf(M, ml[2 * s0]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float L = 0.f;
-  float acc[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-  if (M != kNegInf) {
-#pragma unroll 16
-    for (int s = 0; s < a.splits; ++s) {
-      const float2 st = *(const float2*)(ml + 2 * s);
-      const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
-      L += st.y * w;
-      if constexpr (PL == 2) {
-        const float2 v = *(const float2*)(po + (int64_t)s * D);
-        acc[0] += w * v.x;
-        acc[1] += w * v.y;
-      } else {
-        acc[0] += w * po[(int64_t)s * D];
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  constexpr int C4 = D / 4;
+  constexpr int PARTS = 128 / C4;
+  __shared__ float4 s_acc[256];
+  __shared__ float2 s_ml[256];
+  const int t = threadIdx.x;
+  const int64_t R = (int64_t)blockIdx.x * kCombineRows + t / 128;  // (b * Hkv + h) * rows + r
+  const int64_t rows_total = (int64_t)a.batch * a.Hkv * a.rows;
+  const int d4 = (t & 127) % C4, part = (t & 127) / C4;
+  const int S = a.splits;
+  const int span = (S + PARTS - 1) / PARTS;
+  const int s_lo = min(S, part * span), s_hi = min(S, s_lo + span);
+  float M = kNegInf, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (R < rows_total) {
+    const float2* ml = (const float2*)a.ws_ml + R * S;
+    const float4* po = (const float4*)(a.ws_o + R * S * D) + d4;
+    for (int sp = s_lo; sp < s_hi; ++sp) M = fmaxf(M, ml[sp].x);
+    if (M != kNegInf) {
+#pragma unroll 8
+      for (int sp = s_lo; sp < s_hi; ++sp) {
+        const float2 st = ml[sp];
+        const float4 v = po[(int64_t)sp * C4];
+        const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
+        L += w * st.y;
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
       }
+    }
+  }
+  s_acc[t] = acc;
+  s_ml[t] = make_float2(M, L);
+  __syncthreads();
+  if (R >= rows_total || part != 0) return;
+  float Mt = kNegInf;
+  for (int p = 0; p < PARTS; ++p) Mt = fmaxf(Mt, s_ml[t + p * C4].x);
+  float Lt = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (Mt != kNegInf) {
+    for (int p = 0; p < PARTS; ++p) {
+      const float2 st = s_ml[t + p * C4];
+      const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - Mt);
+      const float4 v = s_acc[t + p * C4];
+      Lt += w * st.y;
+      o.x += w * v.x;
+      o.y += w * v.y;
+      o.z += w * v.z;
+      o.w += w * v.w;
     }
   }
   const int r = (int)(R % a.rows);
   const int64_t bh = R / a.rows;
-  const int h = (int)(bh % a.Hkv);
-  const int b = (int)(bh / a.Hkv);
-  const int i = r / a.G;
-  const int hl = r - i * a.G;
-  const int64_t orow = ((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl;
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) a.out[orow * D + lane * PL + e] = acc[e] * inv;
-  if (a.lse && lane == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
-}
-
-// tiles in flight per wave: eight-wave workgroups run two waves per SIMD, which
-// hide each other's memory latency, so one tile per wave fits their register
-// budget; narrower workgroups keep two.
-template <int D, int RB, int NW>
-constexpr int pipeline_depth() {
-  return (NW >= 8) ? 1 : 2;
+  const int h = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
+  const int qi = r / a.G, hl = r - qi * a.G;
+  const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
+  const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
+  *(float4*)(a.out + orow * D + 4 * d4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (a.lse && d4 == 0) a.lse[orow] = (Lt > 0.f) ? (Mt + log2f(Lt)) * kLn2 : kNegInf;
 }
 
 template <int D, int RB, int NW>
 void launch_rb(const AttnArgs& a, int batch, int row_chunks, hipStream_t st) {
   dim3 grid((unsigned)(batch * a.Hkv * a.splits), (unsigned)row_chunks);
-  attn_splitk<D, RB, NW, pipeline_depth<D, RB, NW>()><<<grid, 64 * NW, 0, st>>>(a);
+  attn_splitk<D, RB, NW, ring_depth<D, RB, NW>()><<<grid, 64 * NW, 0, st>>>(a);
 }
 
 template <int D, int NW>
@@ -465,8 +566,7 @@ void launch_nw(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t
 
 template <int D>
 void launch_d(const AttnArgs& a, int nw, int rb, int batch, int row_chunks, hipStream_t st) {
-  if (nw == 8) launch_nw<D, 8>(a, rb, batch, row_chunks, st);
-  else if (nw == 4) launch_nw<D, 4>(a, rb, batch, row_chunks, st);
+  if (nw == 4) launch_nw<D, 4>(a, rb, batch, row_chunks, st);
   else if (nw == 2) launch_nw<D, 2>(a, rb, batch, row_chunks, st);
   else launch_nw<D, 1>(a, rb, batch, row_chunks, st);
 }
@@ -474,6 +574,8 @@ void launch_d(const AttnArgs& a, int nw, int rb, int batch, int row_chunks, hipS
 struct Plan {
   int rb, row_chunks, nw, splits, keys_per_split;
 };
+
+
 
 Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
   Plan p;
@@ -492,8 +594,22 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
   const int tiles_per_split = (tiles + splits - 1) / splits;
   p.keys_per_split = tiles_per_split * kTile;
   p.splits = (max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
-  p.nw = tiles_per_split >= 8 ? 8 : (tiles_per_split >= 4 ? 4 : (tiles_per_split >= 2 ? 2 : 1));
+  p.nw = tiles_per_split >= 4 ? 4 : (tiles_per_split >= 2 ? 2 : 1);
   return p;
+}
+
+// Workspace layout: the partial outputs, then the partial (max, sum) pairs.
+struct WsLayout {
+  size_t o_off, ml_off, total;
+};
+WsLayout ws_layout(const Plan& p, int batch, int Hq, int nq, int D) {
+  WsLayout w{};
+  if (p.splits <= 1) return w;
+  const size_t rows_total = (size_t)batch * Hq * nq;
+  w.o_off = 0;
+  w.ml_off = w.o_off + rows_total * p.splits * D * sizeof(float);
+  w.total = w.ml_off + rows_total * p.splits * 2 * sizeof(float);
+  return w;
 }
 
 }  // namespace
@@ -505,9 +621,7 @@ extern "C" size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv,
                                              int num_splits) {
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_kv_len < 1) return 0;
   const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
-  if (p.splits <= 1) return 0;
-  const size_t rows_total = (size_t)batch * Hq * nq;
-  return rows_total * p.splits * ((size_t)D + 2) * sizeof(float);
+  return ws_layout(p, batch, Hq, nq, D).total;
 }
 
 extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
@@ -546,6 +660,7 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   a.kv_sn = kv_sn;
   a.kv_len = kv_len;
   a.max_kv_len = max_kv_len;
+  a.batch = batch;
   a.nq = nq;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -557,16 +672,16 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   a.keys_per_split = p.keys_per_split;
   a.out = out;
   a.lse = lse;
-  a.ws_o = (float*)ws;
-  const size_t rows_total = (size_t)batch * Hq * nq;
-  a.ws_ml = ws ? (float*)ws + rows_total * p.splits * D : nullptr;
+  const WsLayout wl = ws_layout(p, batch, Hq, nq, D);
+  a.ws_o = ws ? (float*)((char*)ws + wl.o_off) : nullptr;
+  a.ws_ml = ws ? (float*)((char*)ws + wl.ml_off) : nullptr;
   hipStream_t st = (hipStream_t)stream;
   if (D == 128) launch_d<128>(a, p.nw, p.rb, batch, p.row_chunks, st);
   else launch_d<64>(a, p.nw, p.rb, batch, p.row_chunks, st);
   if (p.splits > 1) {
-    const unsigned blocks = (unsigned)((rows_total + 3) / 4);
-    if (D == 128) attn_combine<128><<<blocks, 256, 0, st>>>(a, (int64_t)rows_total);
-    else attn_combine<64><<<blocks, 256, 0, st>>>(a, (int64_t)rows_total);
+    const unsigned blocks = (unsigned)(((int64_t)batch * Hkv * a.rows + kCombineRows - 1) / kCombineRows);
+    if (D == 128) attn_combine<128><<<blocks, 256, 0, st>>>(a);
+    else attn_combine<64><<<blocks, 256, 0, st>>>(a);
   }
   return check_launch("svlm_decode_attn");
 }

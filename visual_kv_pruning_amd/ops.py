@@ -38,6 +38,7 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+
 # ---------------------------------------------------------------------------
 def score_workspace_bytes(T: int, Hq: int, Hkv: int, q_pos0: int, n_vis: int) -> int:
     return int(L.load().svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis))

@@ -38,6 +38,35 @@ import workloads as W  # noqa: E402
 
 METRIC = "decode-attn µs/step + HBM GB/s (dense verify γ+1, 10% draft) at 25k vis tokens"
 HBM_PEAK_GBS = 8000.0
+# rocprofv3 --pmc summary of the dense-verify call at this workload: HBM bytes per
+# call, taken for the kernel source whose hash it records
+VERIFY_PMC = os.path.join(ROOT, "profiles", "decode_attn_verify_llavaov72b_25k_pmc.txt")
+KERNEL_SOURCES = ("visual_kv_pruning_amd/csrc/decode_attn.hip", "visual_kv_pruning_amd/csrc/svlm_internal.h")
+CALIB_COPY_BYTES = 256 << 20   # plain device copy of known size that scales the PMC byte counters
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per dense-verify call from the committed counter summary, or None
+    when that summary is missing or was taken on a different kernel source."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(VERIFY_PMC).read().splitlines() if ":" in line)
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_call"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -103,6 +132,14 @@ def main():
     o_d = torch.empty(1, 1, Hq, D, dtype=torch.float32, device=dev)
     l_d = torch.empty(1, 1, Hq, dtype=torch.float32, device=dev)
     kept_box = {}
+
+    # one plain copy of known size, untimed: under rocprofv3 --pmc its FETCH_SIZE and
+    # WRITE_SIZE give the scale factor of those counters on this machine
+    calib_src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     def k_score(l):
         ops.score(qt[l], K[l], NV, NV, agg="all", alpha=1.0 / L, beta=0.0 if l == 0 else 1.0, out=row, ws=ws_score)
@@ -225,8 +262,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "svlm_decode_attn dense verify (per launch: 25222 keys x 8 KV heads x 512 B)",
+            "traffic": measured_traffic(),
+            "kernel": "svlm_decode_attn dense verify call (split-K kernel + combine; 25222 keys x 8 KV heads "
+                      "x 512 B = 103.3 MB per call)",
         },
         "kernels": kernels,
     }

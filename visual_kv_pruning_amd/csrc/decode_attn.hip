@@ -8,20 +8,26 @@
 // memory bandwidth (SpecVLM technology-transfer listing, section 4).
 //
 // Design (one wave = 64 lanes; c = lane % 16, g = lane / 16):
-//  * a workgroup owns one (batch, KV head, key split) and up to 80 query rows
-//    (rows = G * nq, row r = i * G + local head), padded to 16-row blocks;
-//  * K and V are read straight from HBM into registers in matrix-core operand
-//    layout, 32 keys per wave per step, double buffered, each byte once;
-//  * S^T = K * Q^T on v_mfma_f32_16x16x32_bf16: lane holds 4 keys x 1 row per
-//    16-key block, so every lane owns one query row throughout;
-//  * online softmax in the exp2 domain (scale * log2 e folded into one fp32
-//    multiply); row maxima cross the four lane groups with two xor-shuffles;
-//  * O^T += V^T * P^T with P split into bf16 hi + lo (two products), which
-//    keeps the weights at ~2^-16 relative error; V^T operands come from the
-//    16-byte V loads by byte permutes (no LDS round trip);
-//  * waves of a workgroup merge through LDS in a fixed order, then either
-//    write the final fp32 output (one split) or a partial (max, sum, output)
-//    that a second kernel merges in split order.
+//  * a workgroup owns one (batch, KV head, key split) and up to 48 query rows
+//    (80 at D = 64; rows = G * nq, row r = i * G + local head), padded to
+//    16-row MFMA blocks; four waves, one workgroup per compute unit;
+//  * wave w takes the 16-key blocks 64 j + 16 w of the split, so the waves stay
+//    balanced; it stages its own blocks HBM -> LDS with LDS-DMA transfers
+//    (range-checked buffer descriptors, nontemporal) through a private ring
+//    of NS slots and reads them with LDS loads the compiler does not track,
+//    so its only memory waits are the kernel's own static vmcnt waits;
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the queries in registers:
+//    lane holds 4 keys x 1 row per 16-key block, so row statistics need two
+//    cross-lane steps (v_permlane16/32_swap);
+//  * online softmax in the exp2 domain with a lazy rescale (the reference
+//    maximum moves only when a block exceeds it by more than 2^8);
+//  * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: the scores already sit in the
+//    B-operand layout; P enters as a bf16 hi + lo pair (two products), so the
+//    weights carry ~2^-16 relative error; V^T operands come from 16-byte V
+//    rows by byte permutes;
+//  * the four waves merge through LDS in a fixed order, then the workgroup
+//    writes either the final fp32 output (one split) or a partial (max, sum,
+//    output) that a second kernel merges in split order.  Deterministic.
 #include <cmath>
 #include <cstdio>
 
@@ -48,9 +54,11 @@ struct AttnArgs {
   float* ws_ml;  // [B*Hkv*rows][splits][2]
 };
 
-constexpr int kTile = 32;      // keys per wave step
-constexpr int kMaxRB64 = 5;    // up to 80 query rows per workgroup at D = 64
-constexpr int kMaxRB128 = 3;   // 48 rows at D = 128 (more would spill registers)
+constexpr int kWaves = 4;                  // waves per workgroup
+constexpr int kBlock = 16;                 // keys per wave per step (one MFMA block)
+constexpr int kStep = kWaves * kBlock;     // keys per workgroup step
+constexpr int kMaxRB128 = 3;               // query row blocks per workgroup at D = 128 (48 rows)
+constexpr int kMaxRB64 = 5;                // 80 rows at D = 64
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is raised
 
@@ -62,9 +70,9 @@ constexpr int kNT = 2;
 template <int DV>
 struct VRaw;
 template <>
-struct VRaw<8> { typedef unsigned __attribute__((ext_vector_type(4))) T; };
+struct VRaw<8> { typedef u32x4 T; };
 template <>
-struct VRaw<4> { typedef unsigned __attribute__((ext_vector_type(2))) T; };
+struct VRaw<4> { typedef u32x2 T; };
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at max).
@@ -75,53 +83,75 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(enc);
   __asm__ volatile("" ::: "memory");
 }
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
-  __asm__ volatile("" ::: "memory");
+
+// LDS reads of one staged key block, issued together and waited for inside
+// the same asm block, so no read is in flight when the outputs are used.  The
+// staging ring is written by LDS-DMA transfers whose completion the kernel
+// tracks with its own vmcnt waits; reads that the compiler cannot see keep it
+// from adding waits on every transfer in flight.  Outputs are early-clobber:
+// a read may complete while later reads of the block are still queued.
+__device__ __forceinline__ void lds_read_b128x8(u32x4 (&d)[8], const unsigned (&a)[8]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_b128x2_b64x4(u32x4 (&k)[2], u32x2 (&v)[4], const unsigned (&a)[6]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b64 %2, %8\n\t"
+      "ds_read_b64 %3, %9\n\t"
+      "ds_read_b64 %4, %10\n\t"
+      "ds_read_b64 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int DV>
-__device__ __forceinline__ typename VRaw<DV>::T load_v(__amdgpu_buffer_rsrc_t rs, int off);
-template <>
-__device__ __forceinline__ VRaw<8>::T load_v<8>(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
-}
-template <>
-__device__ __forceinline__ VRaw<4>::T load_v<4>(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNT);
-}
-
-// Depth of the per-wave staging ring: as many K/V tiles in flight as the LDS
-// (160 KB per CU, one workgroup per CU) holds, with every outstanding transfer
-// countable by the 6-bit vector-memory wait counter.
-template <int D, int RB, int NW>
+// Depth of each wave's staging ring (key blocks in flight per wave): bounded by
+// the LDS (160 KB per compute unit, one workgroup per unit) and by the 6-bit
+// vector-memory wait counter.
+template <int D>
 constexpr int ring_depth() {
-  constexpr int TB = kTile * D * 2;
-  constexpr int NI = TB / 1024;
-  constexpr int RP = RB * 16;
-  constexpr size_t slice_bytes = (size_t)RP * (D + 4) * 4;
-  int best = 1;
-  for (int ns = 1; ns <= 4; ++ns) {
-    const size_t slot = (size_t)NW * ns * TB;
-    const size_t ks = slot > ((NW + 1) / 2) * slice_bytes ? slot : ((NW + 1) / 2) * slice_bytes;
-    const size_t vs = slot > (NW / 2) * slice_bytes ? slot : (NW / 2) * slice_bytes;
-    const size_t lds = ks + vs + (size_t)RP * D * 2 + 2 * (size_t)NW * RP * 4 + 64;
-    if (2 * ns * NI <= 63 && lds <= 160 * 1024) best = ns;
-  }
-  return best;
+  constexpr int QB = kBlock * D * 2;       // bytes of one staged K (or V) block
+  constexpr int TW = 2 * QB / 1024;        // 1 KB transfers per K+V block
+  int ns = 2;
+  while (ns < 8 && (ns + 1) * TW <= 63 && (size_t)kWaves * (ns + 1) * 2 * QB <= 136 * 1024) ++ns;
+  return ns;
 }
 
-template <int D, int RB, int NW, int NS>
-__global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
+// One workgroup = one (batch, KV head, key split, row chunk) with kWaves waves.
+// Wave w takes the 16-key blocks k_begin + 64 j + 16 w of the split against
+// every query row of the chunk (RB blocks of 16 rows), staging its own blocks
+// through a private ring of NS slots in LDS.  The waves' partial states are
+// merged through LDS in wave order at the end.
+template <int D, int RB, int NS>
+__global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   constexpr int KK = D / 32;             // 32-wide d chunks of the QK product
   constexpr int DV = D / 16;             // d values per lane in the PV product
   constexpr int RP = RB * 16;
-  constexpr int ROWB = D * 2;            // bytes of one K or V row in a staged tile
+  constexpr int ROWB = D * 2;            // bytes of one K or V row
   constexpr int CH = ROWB / 16;          // 16-byte chunks per row
-  constexpr int TB = kTile * ROWB;       // bytes of one staged K (or V) tile
-  constexpr int NI = TB / 1024;          // 1 KB transfers per K (or V) tile
+  constexpr int QB = kBlock * ROWB;      // bytes of one staged K (or V) block
+  constexpr int NQ = QB / 1024;          // 1 KB transfers per K (or V) block
+  constexpr int TW = 2 * NQ;             // transfers per K+V block
+  constexpr int SLOT = 2 * QB;           // one ring slot: K block then V block
   constexpr int OSTRIDE = D + 4;         // fp32 elements per merge-slice row
-  typedef typename VRaw<DV>::T vraw_t;
+  static_assert((NS - 1) * TW <= 63 && NS * TW <= 63, "ring depth");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -138,27 +168,20 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   const int n_kv = min(max(a.kv_len[b], 0), a.max_kv_len);
   const int k_begin = s * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, n_kv);
+  // this wave's blocks: keys k_begin + 64 j + 16 wave, j < n_my
+  const int n_my = (k_end > k_begin + kBlock * wave) ? (k_end - k_begin - kBlock * wave + kStep - 1) / kStep : 0;
 
-  // LDS: one K + V staging slot per wave; staged query rows; per-wave row state.
-  // The slot area is reused for the merge slices after the key loop.
-  // K and V slots are distinct objects so the compiler can tell their transfers apart.
-  // NS staging slots per wave form a ring, so NS tiles are in flight per wave.
-  // After the key loop the slots hold the merge slices: the first half of the
-  // slices in kslots, the rest in vslots.
-  constexpr size_t SLOT_BYTES = (size_t)NW * NS * TB;
-  constexpr int NSLICE = NW;
-  constexpr size_t SLICE_BYTES = (size_t)RP * OSTRIDE * 4;
-  constexpr size_t KS_BYTES = SLOT_BYTES > ((NSLICE + 1) / 2) * SLICE_BYTES ? SLOT_BYTES : ((NSLICE + 1) / 2) * SLICE_BYTES;
-  constexpr size_t VS_BYTES = SLOT_BYTES > (NSLICE / 2) * SLICE_BYTES ? SLOT_BYTES : (NSLICE / 2) * SLICE_BYTES;
-  __shared__ __align__(16) unsigned char kslots[KS_BYTES];
-  __shared__ __align__(16) unsigned char vslots[VS_BYTES];
-  __shared__ __align__(16) unsigned char sq[RP * ROWB];  // query rows, chunks swizzled like the KV tiles
-  __shared__ float sm_m[NW][RP];
-  __shared__ float sm_l[NW][RP];
+  // LDS: the waves' staging rings, each reused after its wave's key loop for
+  // that wave's merge slice; per-wave row maxima and sums for the merge.
+  static_assert((size_t)RP * OSTRIDE * 4 <= (size_t)NS * SLOT, "a wave's merge slice fits in its ring");
+  __shared__ __align__(16) unsigned char lds[(size_t)kWaves * NS * SLOT];
+  __shared__ float sm_m[kWaves][RP];
+  __shared__ float sm_l[kWaves][RP];
+  unsigned char* my_ring = lds + (size_t)wave * NS * SLOT;
 
   // Range-checked buffer descriptors over exactly this split's keys: transfers
   // past k_end deliver zeros without touching memory, so every transfer is
-  // issued unconditionally and the wait counts below are static.
+  // issued unconditionally and the wait counts are static.
   const int64_t row_bytes = a.kv_sn * 2;
   const int n_rows = max(k_end - k_begin, 0);
   const int64_t off0 = (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh + (int64_t)k_begin * a.kv_sn;
@@ -167,72 +190,70 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
 
-  unsigned char* kring = kslots + (size_t)wave * NS * TB;
-  unsigned char* vring = vslots + (size_t)wave * NS * TB;
-
-  // Global -> LDS transfer of 32 rows, row-major with 16-byte chunks XOR-swizzled
-  // by row (chunk p of row r holds source chunk p ^ (r % CH)); every lane moves
-  // 16 bytes and lands at slot + 1 KB * i + 16 * lane.  Nontemporal: read once.
-  auto stage = [&](__amdgpu_buffer_rsrc_t rs, unsigned char* slot, int t0) {
-    const int r0 = t0 - k_begin;
+  // Stage block j of this wave (16 K rows, then the same 16 V rows) into ring
+  // slot `slot`: transfer i moves 1 KB = 1024 / ROWB rows, 16-byte chunks
+  // XOR-swizzled by row (chunk p of row r holds source chunk p ^ (r % CH));
+  // lane l lands at slot + 1 KB * i + 16 l.  Nontemporal: each byte is read once.
+  auto stage = [&](int slot, int j) {
+    unsigned char* base = my_ring + slot * SLOT;
+    const int r_first = j * kStep + kBlock * wave;  // first key of the block, relative to k_begin
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = i * (1024 / ROWB) + lane / CH;
-      const int p = lane % CH;
-      const int src = (r0 + r) * (int)row_bytes + ((p ^ (r % CH)) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(slot + i * 1024), 16,
-                                               src, 0, 0, kNT);
-    }
-  };
-  // chunk `ch` of staged row r
-  auto chunk_at = [&](const unsigned char* slot, int r, int ch) { return slot + r * ROWB + ((ch ^ (r % CH)) * 16); };
-
-  // ---- stage the query rows of this workgroup (B operand of S^T = K Q^T) by
-  // LDS DMA, first; rows past the last query read as zeros
-  {
-    const int64_t qbytes = (int64_t)a.nq * a.Hq * D * 2;
-    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.q + (int64_t)b * a.q_sb), (short)0, (int)qbytes, kBufferFlags);
-    constexpr int QI = RP * ROWB / 1024;  // 1 KB transfers for the staged rows
-    for (int i = wave; i < QI; i += NW) {
-      const int rr = i * (1024 / ROWB) + lane / CH;
-      const int p = lane % CH;
-      const int r = row_base + rr;
-      int src = (int)qbytes;  // out of range: zeros
-      if (r < a.rows) {
-        const int qi = r / a.G;
-        const int hl = r - qi * a.G;
-        src = ((qi * a.Hq + h * a.G + hl) * D) * 2 + ((p ^ (rr % CH)) * 16);
+    for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int r = i * (1024 / ROWB) + lane / CH;
+        const int p = lane % CH;
+        const int src = (r_first + r) * (int)row_bytes + ((p ^ (r % CH)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? vrs : krs,
+                                                 (__attribute__((address_space(3))) void*)(base + kv * QB + i * 1024),
+                                                 16, src, 0, 0, kNT);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(sq + i * 1024), 16, src,
-                                               0, 0, 0);
-    }
-  }
+  };
 
-  // this wave's tiles: t = t_first + j * step, j < n_my
-  const int step = kTile * NW;
-  const int t_first = k_begin + kTile * wave;
-  const int n_my = (t_first < k_end) ? (k_end - t_first + step - 1) / step : 0;
-#pragma unroll
-  for (int q = 0; q < NS; ++q) {  // unconditional: past k_end these deliver zeros
-    stage(krs, kring + q * TB, t_first + q * step);
-    stage(vrs, vring + q * TB, t_first + q * step);
-  }
-  wait_vmcnt<2 * NS * NI>();  // this wave's query transfers have landed
+  // ---- query rows in registers (B operand of S^T = K Q^T): lane (c, g4) holds
+  // row c of block rb, d = 32 kk + 8 g4 .. + 7; rows past the chunk read zeros
+  const int64_t qbytes = (int64_t)a.nq * a.Hq * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + (int64_t)b * a.q_sb), (short)0, (int)qbytes, kBufferFlags);
+  u32x4 qreg[RB][KK];
   int lim[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = row_base + rb * 16 + c;
-    const int i = r / a.G;
-    lim[rb] = (r < a.rows) ? min(k_end, a.causal ? n_kv - a.nq + i + 1 : n_kv) : k_end;
+    const bool valid = r < a.rows;
+    const int qi = r / a.G;
+    const int hl = r - qi * a.G;
+    lim[rb] = valid ? min(k_end, a.causal ? n_kv - a.nq + qi + 1 : n_kv) : k_end;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int off = valid ? ((qi * a.Hq + h * a.G + hl) * D + 32 * kk + 8 * g4) * 2 : (int)qbytes;
+      qreg[rb][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+    }
   }
-  // keys every row of this workgroup may see: tiles below this need no mask
-  const int lim_all = min(k_end, a.causal ? n_kv - a.nq + 1 : n_kv);
-  __syncthreads();
+  // keys every row of this workgroup may see: blocks below this need no mask
+  const int lim_all = min(k_end, a.causal ? n_kv - a.nq + row_base / a.G + 1 : n_kv);
+
+  // prologue: this wave's blocks 0 .. NS-1 (past the split: zeros)
+#pragma unroll
+  for (int u = 0; u < NS; ++u) stage(u, u);
+  wait_vmcnt<NS * TW>();  // the query loads, issued first, have landed
+
+  // LDS byte offsets of this lane's operand chunks within a slot:
+  //   K (A of S^T): row c, chunk 4 kk + g4;  V (for A of O^T): rows 4 g4 + i, d 8 c (or 4 c)
+  unsigned koff[KK], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = c * ROWB + (((kk * 4 + g4) ^ (c % CH)) * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g4 + i;
+    if constexpr (D == 128) voff[i] = QB + r * ROWB + ((c ^ (r % CH)) * 16);
+    else voff[i] = QB + r * ROWB + (((c >> 1) ^ (r % CH)) * 16) + (c & 1) * 8;
+  }
+  const unsigned ring0 = lds_addr(my_ring);
 
   // Running state per row (lane row c + 16 rb, uniform over the four lane
   // groups): m_use is the reference maximum in log2 units, raised only when a
-  // tile's maximum exceeds it by more than kRescale, so the weights stay
+  // block's maximum exceeds it by more than kRescale, so the weights stay
   // <= 2^kRescale and the fp32 accumulators are rescaled only rarely.
   float m_use[RB], l_run[RB];
   f32x4 o[DV][RB];
@@ -245,58 +266,57 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
   }
 
   for (int j = 0; j < n_my; ++j) {
-    const int t0 = t_first + j * step;
-    unsigned char* kslot = kring + (j % NS) * TB;
-    unsigned char* vslot = vring + (j % NS) * TB;
-    // Issue order is K(t) V(t) K(t+1) V(t+1) ... K(t+NS-1) V(t+NS-1): K(t) has
-    // landed once at most 2 NS - 1 groups of NI transfers are outstanding.
-    wait_vmcnt<(2 * NS - 1) * NI>();
-    u32x4 kt_[2][KK];
+    const int slot = j % NS;
+    // block j has landed once the NS - 1 younger blocks are all that is outstanding
+    wait_vmcnt<(NS - 1) * TW>();
+    const unsigned base = ring0 + (unsigned)(slot * SLOT);
+    u32x4 kq[KK];
+    typename VRaw<DV>::T vt[4];
+    if constexpr (D == 128) {
+      unsigned ad[8];
+      u32x4 rd[8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int e = 0; e < 4; ++e) ad[e] = base + koff[e];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kt_[kt][kk] = *(const u32x4*)chunk_at(kslot, 16 * kt + c, kk * 4 + g4);
-    wait_lgkmcnt0();
-    stage(krs, kslot, t0 + NS * step);  // K(t+NS): out of range past the last tile, i.e. zeros
+      for (int e = 0; e < 4; ++e) ad[4 + e] = base + voff[e];
+      lds_read_b128x8(rd, ad);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kq[e] = rd[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[e] = __builtin_bit_cast(typename VRaw<DV>::T, rd[4 + e]);
+    } else {
+      unsigned ad[6];
+      u32x4 kd[2];
+      u32x2 vd[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) ad[e] = base + koff[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ad[2 + e] = base + voff[e];
+      lds_read_b128x2_b64x4(kd, vd, ad);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) kq[e] = kd[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[e] = __builtin_bit_cast(typename VRaw<DV>::T, vd[e]);
+    }
+    stage(slot, j + NS);  // refill the slot just read (past the split: zeros)
 
-    // S^T blocks: lane holds keys t0 + 16kt + 4g4 + ii for its row
-    f32x4 sacc[2][RB];
+    // S^T block: lane holds keys key0 + 4 g4 + i of row c + 16 rb
+    const int key0 = k_begin + j * kStep + kBlock * wave;
+    f32x4 sacc[RB];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[kt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const bf16x8 qv = as_bf16x8(*(const u32x4*)chunk_at(sq, rb * 16 + c, kk * 4 + g4));
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc[kt][rb] = mfma16(as_bf16x8(kt_[kt][kk]), qv, sacc[kt][rb]);
-      }
+      for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), sacc[rb]);
 
-    // V(t) has landed once at most 2 NS - 1 groups are outstanding (K(t+NS) included)
-    wait_vmcnt<(2 * NS - 1) * NI>();
-    vraw_t vt[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int r = (jj < 4) ? (4 * g4 + jj) : (16 + 4 * g4 + jj - 4);
-      if constexpr (DV == 8) vt[jj] = *(const vraw_t*)chunk_at(vslot, r, c);
-      else vt[jj] = *(const vraw_t*)(chunk_at(vslot, r, c >> 1) + (c & 1) * 8);
-    }
-    wait_lgkmcnt0();
-    stage(vrs, vslot, t0 + NS * step);
-
-    const bool full = (t0 + kTile <= lim_all);  // wave-uniform
-    float x[RB][8], mx[RB];
+    const bool full = (key0 + kBlock <= lim_all);  // wave-uniform
+    float x[RB][4], mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = sacc[e >> 2][rb][e & 3];
-        x[rb][e] = (full || t0 + 16 * (e >> 2) + 4 * g4 + (e & 3) < lim[rb]) ? v : kNegInf;
-      }
-      float m = fmaxf(fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])),
-                      fmaxf(fmaxf(x[rb][4], x[rb][5]), fmaxf(x[rb][6], x[rb][7])));
+      for (int i = 0; i < 4; ++i) x[rb][i] = (full || key0 + 4 * g4 + i < lim[rb]) ? sacc[rb][i] : kNegInf;
+      const float m = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
       mx[rb] = max_xor32(max_xor16(m)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
     }
     bool grow = false;
@@ -313,165 +333,119 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_splitk(AttnArgs a) {
         m_use[rb] = m_new;
       }
     }
-    bf16x8 phi[RB], plo[RB];
+    // P^T as the B operand of the 16x16x16 product: lane (c, g4) holds
+    // P[row c][keys 4 g4 .. 4 g4 + 3] exactly where the scores are; bf16 hi + lo
+    bf16x4 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float mneg = (m_use[rb] == kNegInf) ? 0.f : -m_use[rb];
-      float p[8];
+      float p[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[rb][e], a.c, mneg));
-      l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      u32x4 hi, lo;
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(x[rb][i], a.c, mneg));
+      l_run[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+      u32x2 hi, lo;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
+      for (int qd = 0; qd < 2; ++qd) {
         const unsigned b0 = f_bits(p[2 * qd]), b1 = f_bits(p[2 * qd + 1]);
         hi[qd] = perm(b1, b0, kPermHi);
         const float r0 = p[2 * qd] - bits_f(b0 & 0xFFFF0000u);
         const float r1 = p[2 * qd + 1] - bits_f(b1 & 0xFFFF0000u);
         lo[qd] = perm(f_bits(r1), f_bits(r0), kPermHi);
       }
-      phi[rb] = as_bf16x8(hi);
-      plo[rb] = as_bf16x8(lo);
+      phi[rb] = as_bf16x4(hi);
+      plo[rb] = as_bf16x4(lo);
     }
-    // O^T += V^T P^T, two column blocks at a time (hi and lo products into one
-    // accumulator are 2 * RB instructions apart)
+    // O^T += V^T P^T: the A operand of d-block mb holds V[keys 4 g4 .. + 3][d = DV c + mb]
 #pragma unroll
-    for (int mb = 0; mb < DV; mb += 2) {
-      bf16x8 vop[2];
+    for (int mb = 0; mb < DV; ++mb) {
+      const int w = mb >> 1;
+      const unsigned sel = (mb & 1) ? kPermHi : kPermLo;
+      u32x2 vv;
+      vv[0] = perm(vt[1][w], vt[0][w], sel);
+      vv[1] = perm(vt[3][w], vt[2][w], sel);
+      const bf16x4 vop = as_bf16x4(vv);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int w = (mb + u) >> 1;
-        const unsigned sel = ((mb + u) & 1) ? kPermHi : kPermLo;
-        u32x4 vv;
+      for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16k16(vop, phi[rb], o[mb][rb]);
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) vv[qd] = perm(vt[2 * qd + 1][w], vt[2 * qd][w], sel);
-        vop[u] = as_bf16x8(vv);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[mb + u][rb] = mfma16(vop[u], phi[rb], o[mb + u][rb]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[mb + u][rb] = mfma16(vop[u], plo[rb], o[mb + u][rb]);
+      for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16k16(vop, plo[rb], o[mb][rb]);
     }
   }
-  wait_vmcnt<0>();  // the zero-filled transfers past the end must land before the slots are reused
+  wait_vmcnt<0>();  // the zero-filled transfers past the end land before the ring is reused
 
-  // row sums: add the four lane groups (the reference maxima are uniform across them)
-  float m_run[RB];
+  // ---- merge the waves: each parks its row maxima, row sums and unscaled
+  // output sums in a slice inside its own staging ring (which only it has
+  // used), so no wave waits for another before writing; after one barrier
+  // every thread weights
+  // and adds the slices of its (row, 4 columns) items in wave order and writes
+  // them with coalesced stores.  All LDS loads of a thread are issued together.
+  {
+    float* my_slice = (float*)my_ring;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] = sum_xor32(sum_xor16(l_run[rb]));
-    m_run[rb] = m_use[rb];
-  }
-
-  // ---- merge the waves of the workgroup: each wave scales its sums to the
-  // common row maximum and parks them in its own LDS slice; then all threads
-  // add the slices in wave order and write the rows with coalesced stores.
-  if constexpr (NW > 1) {
-    if (g4 == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        sm_m[wave][rb * 16 + c] = m_run[rb];
-        sm_l[wave][rb * 16 + c] = l_run[rb];
-      }
-    }
-    __syncthreads();  // every wave is past its key loop: the slot area is reused below
-    auto slice = [&](int k) {
-      constexpr int KH = (NSLICE + 1) / 2;
-      return (k < KH) ? (float*)kslots + (size_t)k * RP * OSTRIDE : (float*)vslots + (size_t)(k - KH) * RP * OSTRIDE;
-    };
-    {
-      float* sl = slice(wave);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 16 + c;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][row]);
-        const float f = (m_run[rb] == kNegInf) ? 0.f : exp2f(m_run[rb] - M);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int mb = 0; mb < DV; mb += 4)
-            *(float4*)(sl + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
-                make_float4(o[mb][rb][i] * f, o[mb + 1][rb][i] * f, o[mb + 2][rb][i] * f, o[mb + 3][rb][i] * f);
-      }
-    }
-    __syncthreads();
-    constexpr int C4 = D / 4;
-    for (int e = threadIdx.x; e < RP * C4; e += 64 * NW) {
-      const int row = e / C4, d4 = e - row * C4;
-      const int r = row_base + row;
-      if (r >= a.rows) continue;
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][row]);
-      float L = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w][row];
-        L += (mw == kNegInf) ? 0.f : sm_l[w][row] * exp2f(mw - M);
-        const float4 v = *(const float4*)(slice(w) + row * OSTRIDE + 4 * d4);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-      }
-      const int qi = r / a.G;
-      const int hl = r - qi * a.G;
-      if (a.splits == 1) {
-        const float inv = (L > 0.f) ? 1.f / L : 0.f;
-        const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
-        *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
-      } else {
-        const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
-        *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
-        if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
-      }
-    }
-  } else {
-    // ---- one wave: write the final output (one split) or this split's partial state
-  #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int r = row_base + rb * 16 + c;
-      if (r >= a.rows) continue;
-      const int i = r / a.G;
-      const int hl = r - i * a.G;
-      if (a.splits == 1) {
-        const float L = l_run[rb];
-        const float inv = (L > 0.f) ? 1.f / L : 0.f;
-        float* orow = a.out + (((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl) * D;
-  #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-  #pragma unroll
-          for (int mb = 0; mb < DV; mb += 4) {
-            float4 vv = make_float4(o[mb][rb][i4] * inv, o[mb + 1][rb][i4] * inv, o[mb + 2][rb][i4] * inv,
-                                    o[mb + 3][rb][i4] * inv);
-            *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
-          }
-        if (a.lse && g4 == 0)
-          a.lse[((int64_t)b * a.nq + i) * a.Hq + (int64_t)h * a.G + hl] =
-              (L > 0.f) ? (m_run[rb] + log2f(L)) * kLn2 : kNegInf;
-      } else {
-        const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
-        float* orow = a.ws_o + (R * a.splits + s) * D;
-  #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-  #pragma unroll
-          for (int mb = 0; mb < DV; mb += 4) {
-            float4 vv = make_float4(o[mb][rb][i4], o[mb + 1][rb][i4], o[mb + 2][rb][i4], o[mb + 3][rb][i4]);
-            *(float4*)(orow + DV * (4 * g4 + i4) + mb) = vv;
-          }
-        if (g4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(m_run[rb], l_run[rb]);
+      l_run[rb] = sum_xor32(sum_xor16(l_run[rb]));
+      const int row = rb * 16 + c;
+      if (g4 == 0) {
+        sm_m[wave][row] = m_use[rb];
+        sm_l[wave][row] = l_run[rb];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mb = 0; mb < DV; mb += 4)
+          *(float4*)(my_slice + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
+              make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
     }
   }
-
+  __syncthreads();  // every wave's slice and row state are in LDS
+  constexpr int C4 = D / 4;
+  constexpr int ITEMS = (RP * C4 + 64 * kWaves - 1) / (64 * kWaves);
+  float4 part[ITEMS][kWaves];
+  float pm[ITEMS][kWaves], pl[ITEMS][kWaves];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int e = min((int)threadIdx.x + k * 64 * kWaves, RP * C4 - 1);
+    const int row = e / C4, d4 = e - row * C4;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      part[k][w] = *(const float4*)((const float*)(lds + (size_t)w * NS * SLOT) + row * OSTRIDE + 4 * d4);
+      pm[k][w] = sm_m[w][row];
+      pl[k][w] = sm_l[w][row];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int e = threadIdx.x + k * 64 * kWaves;
+    if (e >= RP * C4) break;
+    const int row = e / C4, d4 = e - row * C4;
+    const int r = row_base + row;
+    if (r >= a.rows) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pm[k][w]);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = (pm[k][w] == kNegInf) ? 0.f : fast_exp2(pm[k][w] - M);
+      L += f * pl[k][w];
+      acc.x += f * part[k][w].x;
+      acc.y += f * part[k][w].y;
+      acc.z += f * part[k][w].z;
+      acc.w += f * part[k][w].w;
+    }
+    const int qi = r / a.G;
+    const int hl = r - qi * a.G;
+    if (a.splits == 1) {
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
+      *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+    } else {
+      const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
+      *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
+      if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
+    }
+  }
 }
 
 // Separate merge launch for large partial volumes: kCombineRows rows per
@@ -543,58 +517,53 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (a.lse && d4 == 0) a.lse[orow] = (Lt > 0.f) ? (Mt + log2f(Lt)) * kLn2 : kNegInf;
 }
 
-template <int D, int RB, int NW>
+template <int D, int RB>
 void launch_rb(const AttnArgs& a, int batch, int row_chunks, hipStream_t st) {
   dim3 grid((unsigned)(batch * a.Hkv * a.splits), (unsigned)row_chunks);
-  attn_splitk<D, RB, NW, ring_depth<D, RB, NW>()><<<grid, 64 * NW, 0, st>>>(a);
+  attn_splitk<D, RB, ring_depth<D>()><<<grid, 64 * kWaves, 0, st>>>(a);
 }
 
-template <int D, int NW>
-void launch_nw(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t st) {
+template <int D>
+void launch_d(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t st) {
   switch (rb) {
-    case 1: launch_rb<D, 1, NW>(a, batch, row_chunks, st); break;
-    case 2: launch_rb<D, 2, NW>(a, batch, row_chunks, st); break;
-    case 3: launch_rb<D, 3, NW>(a, batch, row_chunks, st); break;
+    case 1: launch_rb<D, 1>(a, batch, row_chunks, st); break;
+    case 2: launch_rb<D, 2>(a, batch, row_chunks, st); break;
+    case 3: launch_rb<D, 3>(a, batch, row_chunks, st); break;
     default:
       if constexpr (D == 64) {
-        if (rb == 4) launch_rb<D, 4, NW>(a, batch, row_chunks, st);
-        else launch_rb<D, 5, NW>(a, batch, row_chunks, st);
+        if (rb == 4) launch_rb<D, 4>(a, batch, row_chunks, st);
+        else launch_rb<D, 5>(a, batch, row_chunks, st);
       }
       break;
   }
 }
 
-template <int D>
-void launch_d(const AttnArgs& a, int nw, int rb, int batch, int row_chunks, hipStream_t st) {
-  if (nw == 4) launch_nw<D, 4>(a, rb, batch, row_chunks, st);
-  else if (nw == 2) launch_nw<D, 2>(a, rb, batch, row_chunks, st);
-  else launch_nw<D, 1>(a, rb, batch, row_chunks, st);
-}
-
 struct Plan {
-  int rb, row_chunks, nw, splits, keys_per_split;
+  int rb, row_chunks, splits, keys_per_split;
 };
 
-
+constexpr int kMinStepsPerSplit = 2;  // shorter splits cost more in fixed latency than they add in parallelism
 
 Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
   Plan p;
   const int rows = (Hq / Hkv) * nq;
   const int max_rb = (D == 128) ? kMaxRB128 : kMaxRB64;
-  p.rb = std::min(max_rb, (rows + 15) / 16);
+  // row blocks per chunk: as few chunks as possible, then as few padded rows
+  const int chunks = (rows + max_rb * 16 - 1) / (max_rb * 16);
+  p.rb = ((rows + chunks - 1) / chunks + 15) / 16;
   p.row_chunks = (rows + p.rb * 16 - 1) / (p.rb * 16);
-  const int tiles = (max_kv_len + kTile - 1) / kTile;
+  const int steps = (max_kv_len + kStep - 1) / kStep;
   int splits = num_splits;
   if (splits <= 0) {
-    // about one workgroup per compute unit
+    // about one workgroup per compute unit, without splits shorter than kMinStepsPerSplit steps
     const int units = std::max(1, batch * Hkv * p.row_chunks);
     splits = std::max(1, (num_cus() + units - 1) / units);
+    splits = std::min(splits, std::max(1, steps / kMinStepsPerSplit));
   }
-  splits = std::max(1, std::min(splits, tiles));
-  const int tiles_per_split = (tiles + splits - 1) / splits;
-  p.keys_per_split = tiles_per_split * kTile;
+  splits = std::max(1, std::min(splits, steps));
+  const int steps_per_split = (steps + splits - 1) / splits;
+  p.keys_per_split = steps_per_split * kStep;
   p.splits = (max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
-  p.nw = tiles_per_split >= 4 ? 4 : (tiles_per_split >= 2 ? 2 : 1);
   return p;
 }
 
@@ -676,8 +645,8 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   a.ws_o = ws ? (float*)((char*)ws + wl.o_off) : nullptr;
   a.ws_ml = ws ? (float*)((char*)ws + wl.ml_off) : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  if (D == 128) launch_d<128>(a, p.nw, p.rb, batch, p.row_chunks, st);
-  else launch_d<64>(a, p.nw, p.rb, batch, p.row_chunks, st);
+  if (D == 128) launch_d<128>(a, p.rb, batch, p.row_chunks, st);
+  else launch_d<64>(a, p.rb, batch, p.row_chunks, st);
   if (p.splits > 1) {
     const unsigned blocks = (unsigned)(((int64_t)batch * Hkv * a.rows + kCombineRows - 1) / kCombineRows);
     if (D == 128) attn_combine<128><<<blocks, 256, 0, st>>>(a);

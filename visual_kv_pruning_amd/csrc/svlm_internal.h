@@ -22,6 +22,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // device side: vector types for the bf16 matrix-core builtins
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 
@@ -30,6 +32,17 @@ typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 //   acc holds C[m = 4g .. 4g+3][n = c].
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_bf16.  Lane l (c = l % 16, g = l / 16):
+//   a holds A[m = c][k = 4g .. 4g+3], b holds B[k = 4g .. 4g+3][n = c],
+//   acc holds C[m = 4g .. 4g+3][n = c].
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 as_bf16x4(const u32x2& v) {
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   static_assert((NS - 1) * TW <= 63 && NS * TW <= 63, "ring depth");
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int c = lane & 15;
   const int g4 = lane >> 4;
 
@@ -193,21 +193,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   // Stage block j of this wave (16 K rows, then the same 16 V rows) into ring
   // slot `slot`: transfer i moves 1 KB = 1024 / ROWB rows, 16-byte chunks
   // XOR-swizzled by row (chunk p of row r holds source chunk p ^ (r % CH));
-  // lane l lands at slot + 1 KB * i + 16 l.  Nontemporal: each byte is read once.
+  // lane l lands at slot + 1 KB * i + 16 l.  The per-lane part of each source
+  // offset is fixed; the block's first row enters as the scalar offset.
+  // Nontemporal: each byte is read once.
+  static_assert(NQ <= 4, "transfers per block");
+  int src_lane[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int r = i * (1024 / ROWB) + lane / CH;
+    const int p = lane % CH;
+    src_lane[i] = r * (int)row_bytes + ((p ^ (r % CH)) * 16);
+  }
   auto stage = [&](int slot, int j) {
     unsigned char* base = my_ring + slot * SLOT;
-    const int r_first = j * kStep + kBlock * wave;  // first key of the block, relative to k_begin
+    const int soff = (j * kStep + kBlock * wave) * (int)row_bytes;  // first row of the block, in bytes
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int r = i * (1024 / ROWB) + lane / CH;
-        const int p = lane % CH;
-        const int src = (r_first + r) * (int)row_bytes + ((p ^ (r % CH)) * 16);
+      for (int i = 0; i < NQ; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? vrs : krs,
                                                  (__attribute__((address_space(3))) void*)(base + kv * QB + i * 1024),
-                                                 16, src, 0, 0, kNT);
-      }
+                                                 16, src_lane[i], soff, 0, kNT);
   };
 
   // ---- query rows in registers (B operand of S^T = K Q^T): lane (c, g4) holds
@@ -265,7 +271,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
     for (int mb = 0; mb < DV; ++mb) o[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int j = 0; j < n_my; ++j) {
+  // One 16-key block of this wave.  `masked` blocks reach some row's causal
+  // or split limit and mask per key; the others (all but the last one or two
+  // of a split) skip the per-key tests.
+  auto block = [&](int j, bool masked) {
     const int slot = j % NS;
     // block j has landed once the NS - 1 younger blocks are all that is outstanding
     wait_vmcnt<(NS - 1) * TW>();
@@ -310,13 +319,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), sacc[rb]);
 
-    const bool full = (key0 + kBlock <= lim_all);  // wave-uniform
     float x[RB][4], mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[rb][i] = (full || key0 + 4 * g4 + i < lim[rb]) ? sacc[rb][i] : kNegInf;
-      const float m = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
+      for (int i = 0; i < 4; ++i) {
+        x[rb][i] = (!masked || key0 + 4 * g4 + i < lim[rb]) ? sacc[rb][i] : kNegInf;
+      }
+      const float m = fmax_nn(fmax_nn(x[rb][0], x[rb][1]), fmax_nn(x[rb][2], x[rb][3]));
       mx[rb] = max_xor32(max_xor16(m)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
     }
     bool grow = false;
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = fmaxf(m_use[rb], mx[rb]);
+        const float m_new = fmax_nn(m_use[rb], mx[rb]);
         const float alpha = (m_use[rb] == kNegInf) ? 0.f : fast_exp2(m_use[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
@@ -369,7 +379,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16k16(vop, plo[rb], o[mb][rb]);
     }
-  }
+  };
+  // blocks below n_full see every key of every row
+  const int full_span = lim_all - k_begin - kBlock * wave - kBlock;  // block j is full iff kStep * j <= full_span
+  const int n_full = min(n_my, full_span >= 0 ? full_span / kStep + 1 : 0);
+  int jb = 0;
+  for (; jb < n_full; ++jb) block(jb, false);
+  for (; jb < n_my; ++jb) block(jb, true);
   wait_vmcnt<0>();  // the zero-filled transfers past the end land before the ring is reused
 
   // ---- merge the waves: each parks its row maxima, row sums and unscaled
@@ -555,9 +571,12 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
   const int steps = (max_kv_len + kStep - 1) / kStep;
   int splits = num_splits;
   if (splits <= 0) {
-    // about one workgroup per compute unit, without splits shorter than kMinStepsPerSplit steps
+    // Workgroups for about three quarters of the compute units: the key loop
+    // is bound by HBM bandwidth well before every unit is busy, while each
+    // extra split adds partial state for the merge.  No split shorter than
+    // kMinStepsPerSplit steps.
     const int units = std::max(1, batch * Hkv * p.row_chunks);
-    splits = std::max(1, (num_cus() + units - 1) / units);
+    splits = std::max(1, (3 * num_cus() / 4 + units - 1) / units);
     splits = std::min(splits, std::max(1, steps / kMinStepsPerSplit));
   }
   splits = std::max(1, std::min(splits, steps));

@@ -62,15 +62,25 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 
+// max(a, b) for non-NaN operands as one v_max_f32: fmaxf would first quiet
+// possible NaNs in every operand it cannot prove canonical (cross-lane
+// results, for one), which doubles the instruction count of a max tree.
+__device__ __forceinline__ float fmax_nn(float a, float b) {
+  float r;
+  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Cross-lane butterflies on the VALU (gfx950 v_permlane16/32_swap): after the
 // swap the two results hold the values of lanes l and l ^ 16 (or l ^ 32).
+// The max forms take non-NaN operands.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
-  return fmaxf(bits_f(r[0]), bits_f(r[1]));
+  return fmax_nn(bits_f(r[0]), bits_f(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
-  return fmaxf(bits_f(r[0]), bits_f(r[1]));
+  return fmax_nn(bits_f(r[0]), bits_f(r[1]));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);

@@ -62,65 +62,12 @@ constexpr int kMaxRB64 = 5;                // 80 rows at D = 64
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is raised
 
-// buffer descriptor word 3 for gfx9-family raw buffer loads (no swizzle, no stride)
-constexpr int kBufferFlags = 0x00020000;
-// cache policy of the streaming KV loads: nontemporal
-constexpr int kNT = 2;
-
 template <int DV>
 struct VRaw;
 template <>
 struct VRaw<8> { typedef u32x4 T; };
 template <>
 struct VRaw<4> { typedef u32x2 T; };
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  constexpr int enc = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-  __builtin_amdgcn_s_waitcnt(enc);
-  __asm__ volatile("" ::: "memory");
-}
-
-// LDS reads of one staged key block, issued together and waited for inside
-// the same asm block, so no read is in flight when the outputs are used.  The
-// staging ring is written by LDS-DMA transfers whose completion the kernel
-// tracks with its own vmcnt waits; reads that the compiler cannot see keep it
-// from adding waits on every transfer in flight.  Outputs are early-clobber:
-// a read may complete while later reads of the block are still queued.
-__device__ __forceinline__ void lds_read_b128x8(u32x4 (&d)[8], const unsigned (&a)[8]) {
-  __asm__ volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-__device__ __forceinline__ void lds_read_b128x2_b64x4(u32x4 (&k)[2], u32x2 (&v)[4], const unsigned (&a)[6]) {
-  __asm__ volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %7\n\t"
-      "ds_read_b64 %2, %8\n\t"
-      "ds_read_b64 %3, %9\n\t"
-      "ds_read_b64 %4, %10\n\t"
-      "ds_read_b64 %5, %11\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
-      : "memory");
-}
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Depth of each wave's staging ring (key blocks in flight per wave): bounded by
 // the LDS (160 KB per compute unit, one workgroup per unit) and by the 6-bit

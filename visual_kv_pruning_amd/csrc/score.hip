@@ -7,16 +7,21 @@
 // never stored (a block-wise attention kernel cannot expose it; two passes
 // can):
 //   pass 1: per (q head, text row) log-sum-exp over the causal key range,
-//           split over key ranges; partial (max, sum) per split;
+//           split over key ranges; partial (reference max, sum) per split;
 //   pass 2: per (q head, visual key range) recompute QK^T, form
 //           P = exp2(c*s - lse2) and sum it over the text rows;
 //   agg:    mean over heads as requested, out = alpha*agg + beta*out.
-// Both passes use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Pass 1
-// computes S^T (lane = one text row x 4 keys), so row statistics stay in the
-// lane; pass 2 computes S (lane = 4 rows x one key), so column sums need
-// only two cross-lane steps.  The workgroups of the G q heads that share a KV
-// head and key range are placed on one XCD so the K tile is read from HBM
-// once and served from that XCD's L2 to the others.
+//
+// A workgroup owns one KV head and one key range, with one wave per q head of
+// the KV group (up to 8).  The key tile (64 keys) is staged HBM -> LDS once by
+// LDS-DMA transfers that all waves share (one barrier per tile), so K is read
+// from memory once per workgroup; the text queries of a wave's head sit in
+// registers.  Both passes use v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+// pass 1 computes S^T (lane = one text row x 4 keys per 16-key block) and keeps
+// a lazily raised reference maximum per lane group, so a key costs one fma,
+// one exp2 and one add; pass 2 computes S (lane = 4 text rows x one key), so a
+// column sum over the rows needs two cross-lane steps per tile, and the waves
+// add their heads through LDS.  Exp throughput bounds both passes.
 #include <cmath>
 
 #include "svlm_internal.h"
@@ -25,6 +30,9 @@ namespace svlm {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
+constexpr int kTileKeys = 64;      // keys per staged K tile
+constexpr float kRescale = 8.f;    // log2 headroom before a row's reference maximum is raised
+constexpr int kLseBatch = 16;      // pass-1 partials loaded at once when a row's log-sum-exp is formed
 
 struct ScoreArgs {
   const uint16_t* q;
@@ -32,301 +40,472 @@ struct ScoreArgs {
   const uint16_t* k;
   int64_t k_sh, k_sn;
   int T, n_ctx, q_pos0, vis_start, n_vis, Hq, Hkv, G;
+  int HG1, HG2;  // head groups (workgroups) per KV head, pass 1 and pass 2
   float c;  // scale * log2(e), > 0
   int S1, kps1, S2, kps2;
-  int remap1, remap2;
-  float* ml;    // [Hq][T][S1][2] raw (max, sum)
-  float* head;  // [Hq][n_vis]
+  float* ml;   // [Hq][T][S1][2]: per split, (reference maximum in raw-score units, sum)
+  float* grp;  // [Hkv * HG][n_vis]: per head group, the sum over its heads of the column means
   int agg;
   float alpha, beta;
   float* out;
 };
 
-// block id -> (q head, split); with remap the G q heads of a (split, KV head)
-// group share id % 8, i.e. one XCD
-__device__ __forceinline__ void decode_block(int id, int S, int Hkv, int G, int remap, int& h, int& s) {
-  if (remap) {
-    const int x = id & 7, slot = id >> 3;
-    const int hl = slot % G;
-    const int q = (slot / G) * 8 + x;  // group = s * Hkv + g
-    s = q / Hkv;
-    h = (q % Hkv) * G + hl;
-  } else {
-    h = id % (Hkv * G);
-    s = id / (Hkv * G);
-  }
+// block id -> (KV head g, head group hg, key split s).  Workgroups are handed
+// to the eight XCDs round-robin by id, so the HG head groups of one (KV head,
+// split) take ids 8 apart: they run on one XCD, and the K tiles one of them
+// fetches reach the others from that XCD's L2.  Ids past the last (g, s) pair
+// of a partial group of eight are idle.
+__device__ __forceinline__ bool decode_block(int S, int Hkv, int HG, int& g, int& hg, int& s) {
+  const int bid = blockIdx.x;
+  const int rest = bid >> 3;
+  hg = rest % HG;
+  const int pair = (rest / HG) * 8 + (bid & 7);
+  if (pair >= Hkv * S) return false;
+  s = pair % S;
+  g = pair / S;
+  return true;
 }
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2, float c) {
   const float M = fmaxf(m, m2);
   if (M == kNegInf) return;
-  const float a1 = (m == kNegInf) ? 0.f : l * exp2f((m - M) * c);
-  const float a2 = (m2 == kNegInf) ? 0.f : l2 * exp2f((m2 - M) * c);
+  const float a1 = (m == kNegInf) ? 0.f : l * fast_exp2((m - M) * c);
+  const float a2 = (m2 == kNegInf) ? 0.f : l2 * fast_exp2((m2 - M) * c);
   m = M;
   l = a1 + a2;
 }
 
-template <int D, int RB>
-__device__ __forceinline__ void load_q(const ScoreArgs& a, int h, bf16x8 (&qop)[RB][D / 32]) {
-  const int lane = threadIdx.x & 63, c = lane & 15, g4 = lane >> 4;
+// Ring depth of the shared K tiles: a wave issues PW transfers per tile and
+// at most NS - 1 tiles are outstanding (6-bit wait counter); LDS holds NS tiles.
+template <int D, int W>
+constexpr int score_ring_depth() {
+  constexpr int TB = kTileKeys * D * 2;
+  constexpr int PW = (TB / 1024) / W;
+  int ns = 2;
+  while (ns < 8 && ns * PW <= 63 && (size_t)(ns + 1) * TB <= 128 * 1024) ++ns;
+  return ns;
+}
+
+// Staging of the K tiles of one (KV head, key range) through a ring of NS
+// slots in LDS: every wave issues its share (PW transfers of 1 KB) of each
+// tile; rows are XOR-swizzled by 16-byte chunk (chunk p of row r holds source
+// chunk p ^ (r % CH)).  Tiles past the range deliver zeros.
+template <int D, int W, int NS>
+struct KRing {
+  static constexpr int ROWB = D * 2, CH = ROWB / 16;
+  static constexpr int TB = kTileKeys * ROWB;
+  static constexpr int NI = TB / 1024;
+  static constexpr int PW = NI / W;
+  static_assert(PW >= 1 && NI % W == 0, "tile transfers must split evenly over the waves");
+  static_assert((NS - 1) * PW <= 63, "ring depth");
+  __amdgpu_buffer_rsrc_t rs;
+  unsigned char* lds;
+  int wave, row_bytes;
+  int src_lane[4] = {0, 0, 0, 0};
+
+  __device__ void init(const uint16_t* k_rows, int n_rows, int64_t k_sn, unsigned char* ring, int w) {
+    const int lane = threadIdx.x & 63;
+    row_bytes = (int)(k_sn * 2);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)k_rows, (short)0, n_rows * row_bytes, kBufferFlags);
+    lds = ring;
+    wave = w;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int r = (wave * PW + i) * (1024 / ROWB) + lane / CH;
+      const int p = lane % CH;
+      src_lane[i] = r * row_bytes + ((p ^ (r % CH)) * 16);
+    }
+  }
+  __device__ void stage(int slot, int tile) const {
+    const int soff = tile * kTileKeys * row_bytes;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + slot * TB + (wave * PW + i) * 1024), 16, src_lane[i],
+          soff, 0, kNT);
+  }
+  // LDS byte offset (within a slot) of the lane's K operand chunk: key row r, d chunk kk*4 + g4
+  static __device__ unsigned koff(int r, int kk, int g4) { return r * ROWB + (((kk * 4 + g4) ^ (r % CH)) * 16); }
+};
+
+// the KK K-operand chunks of one 16-key block of a staged tile
+template <int KK>
+__device__ __forceinline__ void read_k_block(unsigned base, const unsigned (&ko)[KK], u32x4 (&kq)[KK]) {
+  unsigned ad[KK];
+#pragma unroll
+  for (int e = 0; e < KK; ++e) ad[e] = base + ko[e];
+  if constexpr (KK == 4) lds_read_b128x4(kq, ad);
+  else lds_read_b128x2(kq, ad);
+}
+
+// S = Q K^T for two 16-key blocks and every text row block (lane: rows
+// 16 rb + 4 g4 + i, key c of each block)
+template <int RB, int KK>
+__device__ __forceinline__ void qk_half(const u32x4 (&q)[RB][KK], const u32x4 (&kq)[2][KK], f32x4 (&S)[RB][2]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int t = rb * 16 + c;
-    if (t < a.T) {
-      const uint16_t* qr = a.q + (int64_t)t * a.q_st + (int64_t)h * a.q_sh + g4 * 8;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) qop[rb][kk] = as_bf16x8(*(const u32x4*)(qr + kk * 32));
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) qop[rb][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[0][kk]), s0);
+      s1 = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[1][kk]), s1);
     }
+    S[rb][0] = s0;
+    S[rb][1] = s1;
   }
 }
 
-// K operand of a 16-key block: lane holds K[key t0 + c][32 kk + 8 g4 .. +8]
-template <int D>
-__device__ __forceinline__ void load_k(const uint16_t* kb, int64_t k_sn, int key, u32x4 (&kop)[D / 32]) {
-  const int g4 = (threadIdx.x & 63) >> 4;
-  const uint16_t* kr = kb + (int64_t)key * k_sn + g4 * 8;
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kop[kk] = *(const u32x4*)(kr + kk * 32);
-}
-
-template <int D, int RB, int NW>
-__global__ __launch_bounds__(64 * NW, (RB >= 8 ? 1 : 2)) void score_pass1(ScoreArgs a) {
-  constexpr int KK = D / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g4 = lane >> 4;
-  int h, s;
-  decode_block(blockIdx.x, a.S1, a.Hkv, a.G, a.remap1, h, s);
-  const int g = h / a.G;
-  bf16x8 qop[RB][KK];
-  load_q<D, RB>(a, h, qop);
-  int lim[RB];  // keys < lim visible to the lane's row
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int t = rb * 16 + c;
-    lim[rb] = (t < a.T) ? a.q_pos0 + t + 1 : 0;
-  }
-  const int k_begin = s * a.kps1;
-  const int k_end = min(k_begin + a.kps1, a.q_pos0 + a.T);
-  const int all_vis_end = min(k_end, a.q_pos0 + 1);  // keys every text row sees
-  const uint16_t* kb = a.k + (int64_t)g * a.k_sh;
-  float m[RB], l[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = kNegInf;
-    l[rb] = 0.f;
-  }
-
-  auto step = [&](const u32x4 (&k0)[KK], const u32x4 (&k1)[KK], int t0) {
-    f32x4 sacc[2][RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        x0 = mfma16(as_bf16x8(k0[kk]), qop[rb][kk], x0);
-        x1 = mfma16(as_bf16x8(k1[kk]), qop[rb][kk], x1);
-      }
-      sacc[0][rb] = x0;
-      sacc[1][rb] = x1;
-    }
-    const bool masked = (t0 + 32 > all_vis_end);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float raw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        raw[e] = sacc[e >> 2][rb][e & 3];
-        if (masked) {
-          const int key = t0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
-          if (key >= lim[rb] || key >= k_end) raw[e] = kNegInf;
-        }
-      }
-      float lmax = raw[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, raw[e]);
-      const float m_new = fmaxf(m[rb], lmax);
-      const float mc = (m_new == kNegInf) ? 0.f : m_new * a.c;
-      const float alpha = fast_exp2(m[rb] * a.c - mc);
-      float sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum += fast_exp2(fmaf(raw[e], a.c, -mc));
-      l[rb] = l[rb] * alpha + sum;
-      m[rb] = m_new;
-    }
-  };
-
-  {
-    const int stride = 32 * NW;
-    int t0 = k_begin + 32 * wave;
-    u32x4 a0[KK], a1[KK], b0[KK], b1[KK];
-    if (t0 < k_end) {
-      load_k<D>(kb, a.k_sn, min(t0 + c, k_end - 1), a0);
-      load_k<D>(kb, a.k_sn, min(t0 + 16 + c, k_end - 1), a1);
-    }
-    while (t0 < k_end) {
-      int tn = t0 + stride;
-      if (tn < k_end) {
-        load_k<D>(kb, a.k_sn, min(tn + c, k_end - 1), b0);
-        load_k<D>(kb, a.k_sn, min(tn + 16 + c, k_end - 1), b1);
-      }
-      step(a0, a1, t0);
-      t0 = tn;
-      if (t0 >= k_end) break;
-      tn = t0 + stride;
-      if (tn < k_end) {
-        load_k<D>(kb, a.k_sn, min(tn + c, k_end - 1), a0);
-        load_k<D>(kb, a.k_sn, min(tn + 16 + c, k_end - 1), a1);
-      }
-      step(b0, b1, t0);
-      t0 = tn;
-    }
-  }
-
-  // merge the four lane groups, then the waves (fixed order)
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    merge_ml(m[rb], l[rb], __shfl_xor(m[rb], 16), __shfl_xor(l[rb], 16), a.c);
-    merge_ml(m[rb], l[rb], __shfl_xor(m[rb], 32), __shfl_xor(l[rb], 32), a.c);
-  }
-  __shared__ float sm[NW][RB * 16][2];
-  if (g4 == 0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      sm[wave][rb * 16 + c][0] = m[rb];
-      sm[wave][rb * 16 + c][1] = l[rb];
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < a.T; t += 64 * NW) {
-    float M = sm[0][t][0], L = sm[0][t][1];
-    for (int w = 1; w < NW; ++w) merge_ml(M, L, sm[w][t][0], sm[w][t][1], a.c);
-    *(float2*)(a.ml + (((int64_t)h * a.T + t) * a.S1 + s) * 2) = make_float2(M, L);
-  }
-}
-
-template <int D, int RB, int NW>
-__global__ __launch_bounds__(64 * NW, (RB >= 8 ? 1 : 2)) void score_pass2(ScoreArgs a) {
-  constexpr int KK = D / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g4 = lane >> 4;
-  int h, s;
-  decode_block(blockIdx.x, a.S2, a.Hkv, a.G, a.remap2, h, s);
-  const int g = h / a.G;
-
-  // row log-sum-exp (log2 units, scaled) from the pass-1 partials, in split order
-  __shared__ float sm_lse[RB * 16];
-  for (int t = threadIdx.x; t < RB * 16; t += 64 * NW) {
-    float v = INFINITY;  // padded rows contribute exp2(-inf) = 0
-    if (t < a.T) {
-      const float* p = a.ml + ((int64_t)h * a.T + t) * a.S1 * 2;
-      float M = p[0], L = p[1];
-      for (int sp = 1; sp < a.S1; ++sp) merge_ml(M, L, p[2 * sp], p[2 * sp + 1], a.c);
-      v = M * a.c + log2f(L);
-    }
-    sm_lse[t] = v;
-  }
-  bf16x8 qop[RB][KK];
-  load_q<D, RB>(a, h, qop);
-  __syncthreads();
-  float lse[RB][4];  // rows 16 rb + 4 g4 + ii
+// the lane's part of the column sums of P = exp2(c s - lse) for the two key blocks
+template <int RB>
+__device__ __forceinline__ void colsum_half(const f32x4 (&S)[RB][2], const float (&lse)[RB][4], float c, float& c0,
+                                            float& c1) {
+  c0 = 0.f;
+  c1 = 0.f;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) lse[rb][ii] = sm_lse[rb * 16 + 4 * g4 + ii];
-
-  const float invT = 1.f / (float)a.T;
-  const int v_begin = a.vis_start + s * a.kps2;
-  const int v_end = min(v_begin + a.kps2, a.vis_start + a.n_vis);
-  const uint16_t* kb = a.k + (int64_t)g * a.k_sh;
-  float* hrow = a.head + (int64_t)h * a.n_vis - a.vis_start;
-
-  auto step = [&](const u32x4 (&k0)[KK], const u32x4 (&k1)[KK], int t0) {
-    float col0 = 0.f, col1 = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        x0 = mfma16(qop[rb][kk], as_bf16x8(k0[kk]), x0);
-        x1 = mfma16(qop[rb][kk], as_bf16x8(k1[kk]), x1);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        col0 += fast_exp2(fmaf(x0[ii], a.c, -lse[rb][ii]));
-        col1 += fast_exp2(fmaf(x1[ii], a.c, -lse[rb][ii]));
-      }
+    for (int i = 0; i < 4; ++i) {
+      c0 += fast_exp2(fmaf(S[rb][0][i], c, -lse[rb][i]));
+      c1 += fast_exp2(fmaf(S[rb][1][i], c, -lse[rb][i]));
     }
-    col0 += __shfl_xor(col0, 16);
-    col1 += __shfl_xor(col1, 16);
-    col0 += __shfl_xor(col0, 32);
-    col1 += __shfl_xor(col1, 32);
-    if (g4 == 0) {
-      if (t0 + c < v_end) hrow[t0 + c] = col0 * invT;
-      if (t0 + 16 + c < v_end) hrow[t0 + 16 + c] = col1 * invT;
-    }
-  };
+}
 
-  {
-    const int stride = 32 * NW;
-    int t0 = v_begin + 32 * wave;
-    u32x4 a0[KK], a1[KK], b0[KK], b1[KK];
-    if (t0 < v_end) {
-      load_k<D>(kb, a.k_sn, min(t0 + c, v_end - 1), a0);
-      load_k<D>(kb, a.k_sn, min(t0 + 16 + c, v_end - 1), a1);
-    }
-    while (t0 < v_end) {
-      int tn = t0 + stride;
-      if (tn < v_end) {
-        load_k<D>(kb, a.k_sn, min(tn + c, v_end - 1), b0);
-        load_k<D>(kb, a.k_sn, min(tn + 16 + c, v_end - 1), b1);
-      }
-      step(a0, a1, t0);
-      t0 = tn;
-      if (t0 >= v_end) break;
-      tn = t0 + stride;
-      if (tn < v_end) {
-        load_k<D>(kb, a.k_sn, min(tn + c, v_end - 1), a0);
-        load_k<D>(kb, a.k_sn, min(tn + 16 + c, v_end - 1), a1);
-      }
-      step(b0, b1, t0);
-      t0 = tn;
+// the 2 * KK K-operand chunks of key blocks kb0, kb0 + 1 of a staged tile
+template <int KK, int BLOCK_BYTES>
+__device__ __forceinline__ void read_k_pair(unsigned base, const unsigned (&ko)[KK], u32x4 (&kq)[2][KK]) {
+  if constexpr (KK == 4) {
+    unsigned ad[8];
+    u32x4 d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ad[e] = base + ko[e % 4] + (e / 4) * BLOCK_BYTES;
+    lds_read_b128x8(d, ad);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kq[e / 4][e % 4] = d[e];
+  } else {
+    unsigned ad[4];
+    u32x4 d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ad[e] = base + ko[e % 2] + (e / 2) * BLOCK_BYTES;
+    lds_read_b128x4(d, ad);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kq[e / 2][e % 2] = d[e];
+  }
+}
+
+// this wave's head's text queries: lane (c, g4) holds row 16 rb + c, d = 32 kk + 8 g4 .. + 7
+// (rows past T read zeros)
+template <int D, int RB>
+__device__ __forceinline__ void load_q(const ScoreArgs& a, int h, u32x4 (&q)[RB][D / 32]) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g4 = lane >> 4;
+  const int bytes = (int)(((int64_t)(a.T - 1) * a.q_st + D) * 2);
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + (int64_t)h * a.q_sh), (short)0, bytes, kBufferFlags);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int t = rb * 16 + c;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const int off = (t < a.T) ? (int)(((int64_t)t * a.q_st + 32 * kk + 8 * g4) * 2) : bytes;
+      q[rb][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
     }
   }
 }
 
+template <int D, int RB, int W, int NS>
+__global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
+  constexpr int KK = D / 32;
+  using Ring = KRing<D, W, NS>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g4 = lane >> 4;
+  int g, hg, s;
+  if (!decode_block(a.S1, a.Hkv, a.HG1, g, hg, s)) return;
+  const int hl = hg * W + wave;  // head within the KV group; waves past the group compute but do not write
+  const int h = g * a.G + min(hl, a.G - 1);
+
+  const int k_begin = s * a.kps1;
+  const int k_end = min(k_begin + a.kps1, a.q_pos0 + a.T);
+  const int n_tiles = (k_end > k_begin) ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+
+  __shared__ __align__(16) unsigned char ring[NS * Ring::TB];
+  Ring kr;
+  kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)k_begin * a.k_sn, max(k_end - k_begin, 0), a.k_sn, ring, wave);
+
+  u32x4 qreg[RB][KK];
+  load_q<D, RB>(a, h, qreg);
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
+  wait_vmcnt<(NS - 1) * Ring::PW>();  // the query loads, issued first, have landed
+
+  // tiles below n_full are visible to every row and lie inside the range
+  const int vis_all = min(k_end, a.q_pos0 + 1) - k_begin;
+  const int n_full = min(n_tiles, vis_all > 0 ? vis_all / kTileKeys : 0);
+  // LDS offsets of the lane's K chunks in key block 0 (block 1 is 16 rows on)
+  unsigned ko[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
+  const unsigned ring0 = lds_addr(ring);
+
+  // per lane group: reference maximum in log2 units of the scaled score, sum
+  float mc[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mc[rb] = kNegInf;
+    l[rb] = 0.f;
+  }
+
+  auto tile = [&](int t, bool masked) {
+    wait_vmcnt<(NS - 2) * Ring::PW>();  // this wave's share of tile t has landed
+    wg_barrier();                       // every share of tile t has landed; tile t-1 is retired
+    kr.stage((t + NS - 1) % NS, t + NS - 1);
+    const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {  // one 16-key block at a time keeps the live registers low
+      u32x4 kq[KK];
+      read_k_block<KK>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq);
+      const int key0 = k_begin + t * kTileKeys + 16 * kb;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s0 = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), s0);
+        float x[4];
+        if (masked) {
+          const int tq = rb * 16 + c;
+          const int lim = min(k_end, (tq < a.T) ? a.q_pos0 + tq + 1 : 0);  // keys < lim visible to the row
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (key0 + 4 * g4 + e < lim) ? s0[e] : kNegInf;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = s0[e];
+        }
+        const float lmax = fmax_nn(fmax3_nn(x[0], x[1], x[2]), x[3]) * a.c;
+        if (lmax > mc[rb] + kRescale) {  // per lane; after the first block only when a row's max jumps
+          const float m_new = fmax_nn(mc[rb], lmax);
+          l[rb] *= (mc[rb] == kNegInf) ? 0.f : fast_exp2(mc[rb] - m_new);
+          mc[rb] = m_new;
+        }
+        const float mneg = (mc[rb] == kNegInf) ? 0.f : -mc[rb];
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
+        l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+    }
+  };
+  int t = 0;
+  for (; t < n_full; ++t) tile(t, false);
+  for (; t < n_tiles; ++t) tile(t, true);
+  wait_vmcnt<0>();
+
+  // merge the four lane groups (fixed order) and write this split's row state
+  // (maximum back in raw-score units)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float m = (mc[rb] == kNegInf) ? kNegInf : mc[rb] / a.c, ll = l[rb];
+    {
+      const auto mr = __builtin_amdgcn_permlane16_swap(f_bits(m), f_bits(m), false, false);
+      const auto lr = __builtin_amdgcn_permlane16_swap(f_bits(ll), f_bits(ll), false, false);
+      float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
+      merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
+      m = m0;
+      ll = l0;
+    }
+    {
+      const auto mr = __builtin_amdgcn_permlane32_swap(f_bits(m), f_bits(m), false, false);
+      const auto lr = __builtin_amdgcn_permlane32_swap(f_bits(ll), f_bits(ll), false, false);
+      float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
+      merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
+      m = m0;
+      ll = l0;
+    }
+    const int tq = rb * 16 + c;
+    if (g4 == 0 && hl < a.G && tq < a.T)
+      *(float2*)(a.ml + (((int64_t)h * a.T + tq) * a.S1 + s) * 2) = make_float2(m, ll);
+  }
+}
+
+template <int D, int RB, int W, int NS>
+__global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
+  constexpr int KK = D / 32;
+  using Ring = KRing<D, W, NS>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g4 = lane >> 4;
+  int g, hg, s;
+  if (!decode_block(a.S2, a.Hkv, a.HG2, g, hg, s)) return;
+  const int hl = hg * W + wave;
+  const bool active = hl < a.G;
+  const int h = g * a.G + min(hl, a.G - 1);
+
+  const int v_begin = a.vis_start + s * a.kps2;
+  const int v_end = min(v_begin + a.kps2, a.vis_start + a.n_vis);
+  const int n_tiles = (v_end > v_begin) ? (v_end - v_begin + kTileKeys - 1) / kTileKeys : 0;
+
+  __shared__ __align__(16) unsigned char ring[NS * Ring::TB];
+  __shared__ float sm_lse[W][RB * 16];
+  __shared__ float xch[2][W][kTileKeys];
+  Ring kr;
+  kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)v_begin * a.k_sn, max(v_end - v_begin, 0), a.k_sn, ring, wave);
+
+  u32x4 qreg[RB][KK];
+  load_q<D, RB>(a, h, qreg);
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
+
+  // row log-sum-exp (log2 units of the scaled score) from the pass-1 partials,
+  // in split order; padded rows get +inf and so contribute exp2(-inf) = 0
+  // (the partials are loaded kLseBatch splits at a time, so a row costs
+  // ceil(S1 / kLseBatch) memory round trips rather than S1)
+  for (int tq = lane; tq < RB * 16; tq += 64) {
+    float v = INFINITY;
+    if (tq < a.T) {
+      const float2* p = (const float2*)(a.ml + ((int64_t)h * a.T + tq) * a.S1 * 2);
+      float M = kNegInf, L = 0.f;
+      for (int s0 = 0; s0 < a.S1; s0 += kLseBatch) {
+        float2 part[kLseBatch];
+#pragma unroll
+        for (int j = 0; j < kLseBatch; ++j) part[j] = (s0 + j < a.S1) ? p[s0 + j] : make_float2(kNegInf, 0.f);
+#pragma unroll
+        for (int j = 0; j < kLseBatch; ++j) merge_ml(M, L, part[j].x, part[j].y, a.c);
+      }
+      v = (L > 0.f) ? M * a.c + log2f(L) : INFINITY;
+    }
+    sm_lse[wave][tq] = v;
+  }
+  wait_lgkmcnt0();
+  float lse[RB][4];  // rows 16 rb + 4 g4 + i
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse[rb][i] = sm_lse[wave][rb * 16 + 4 * g4 + i];
+
+  unsigned ko[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
+  const unsigned ring0 = lds_addr(ring);
+  const float invT = 1.f / (float)a.T;
+  const bool direct = (a.agg == SVLM_AGG_QHEAD) || (a.agg == SVLM_AGG_KVHEAD && a.HG2 == 1);
+  // the KV-head mean is taken here when one workgroup holds the whole group, else by score_agg
+  const float grp_scale = (direct && a.agg == SVLM_AGG_KVHEAD) ? 1.f / (float)a.G : 1.f;
+
+  // writes one output element: the head row (q-head aggregation), the KV-head row
+  // when one workgroup holds the whole group, else the group sum for the final mean
+  auto emit = [&](int row, int key, float v) {
+    const int i = key - a.vis_start;
+    if (direct) {
+      float* o = a.out + (int64_t)row * a.n_vis + i;
+      *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * (*o);
+    } else {
+      a.grp[(int64_t)row * a.n_vis + i] = v;
+    }
+  };
+  // wave 0 adds the waves' column means of tile tt (published in xch[tt % 2])
+  auto flush = [&](int tt) {
+    if (wave != 0) return;
+    const int key = v_begin + tt * kTileKeys + lane;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += xch[tt & 1][w][lane];
+    if (key < v_end) emit(direct ? g : g * a.HG2 + hg, key, v * grp_scale);
+  };
+
+  wait_vmcnt<(NS - 1) * Ring::PW>();  // the query loads, issued first, have landed
+  for (int t = 0; t < n_tiles; ++t) {
+    wait_vmcnt<(NS - 2) * Ring::PW>();
+    wait_lgkmcnt0();  // this wave's column means of tile t-1 are in LDS
+    wg_barrier();
+    kr.stage((t + NS - 1) % NS, t + NS - 1);
+    if (a.agg != SVLM_AGG_QHEAD && t > 0) flush(t - 1);
+    const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
+    float col[4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4 kq[2][KK];
+      read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(hf * 32 * Ring::ROWB), ko, kq);
+      f32x4 S[RB][2];
+      qk_half<RB, KK>(qreg, kq, S);
+      colsum_half<RB>(S, lse, a.c, col[2 * hf], col[2 * hf + 1]);
+    }
+    // column sums over the rows held by the four lane groups; lane (c, g4) then
+    // keeps key 16 g4 + c of the tile
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) col[kb] = sum_xor32(sum_xor16(col[kb]));
+    const float v = ((g4 == 0) ? col[0] : (g4 == 1) ? col[1] : (g4 == 2) ? col[2] : col[3]) * invT;
+    const int key = v_begin + t * kTileKeys + 16 * g4 + c;
+    if (a.agg == SVLM_AGG_QHEAD) {
+      if (active && key < v_end) emit(h, key, v);
+    } else {
+      xch[t & 1][wave][16 * g4 + c] = active ? v : 0.f;
+    }
+  }
+  wait_vmcnt<0>();
+  if (a.agg != SVLM_AGG_QHEAD && n_tiles > 0) {
+    wait_lgkmcnt0();
+    wg_barrier();
+    flush(n_tiles - 1);
+  }
+}
+
+// final mean over the group sums (KV-head rows split over several workgroups,
+// or the single all-head row), out = alpha * mean + beta * out
 __global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int r = blockIdx.y;
   if (i >= a.n_vis) return;
-  int h0, nh;
-  if (a.agg == SVLM_AGG_QHEAD) { h0 = r; nh = 1; }
-  else if (a.agg == SVLM_AGG_KVHEAD) { h0 = r * a.G; nh = a.G; }
-  else { h0 = 0; nh = a.Hq; }
+  int r0, nr;
+  float div;
+  if (a.agg == SVLM_AGG_KVHEAD) {
+    r0 = r * a.HG2;
+    nr = a.HG2;
+    div = (float)a.G;
+  } else {
+    r0 = 0;
+    nr = a.Hkv * a.HG2;
+    div = (float)a.Hq;
+  }
   float acc = 0.f;
-  for (int hh = 0; hh < nh; ++hh) acc += a.head[(int64_t)(h0 + hh) * a.n_vis + i];
-  const float v = acc / (float)nh;
+  for (int k = 0; k < nr; ++k) acc += a.grp[(int64_t)(r0 + k) * a.n_vis + i];
+  const float v = acc / div;
   float* o = a.out + (int64_t)r * a.n_vis + i;
   *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * (*o);
 }
 
+// (g, s) pairs in groups of 8 (one per XCD), times the head groups
+inline unsigned pass_blocks(int Hkv, int S, int HG) { return (unsigned)((Hkv * S + 7) / 8 * 8 * HG); }
+
+template <int D, int RB, int W>
+void launch_pass1(const ScoreArgs& a, hipStream_t st) {
+  score_pass1<D, RB, W, score_ring_depth<D, W>()><<<pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
+}
+template <int D, int RB, int W>
+void launch_pass2(const ScoreArgs& a, hipStream_t st) {
+  score_pass2<D, RB, W, score_ring_depth<D, W>()><<<pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
+}
+
 template <int D, int RB>
-void launch_passes(const ScoreArgs& a, hipStream_t st) {
-  constexpr int NW = 4;
-  score_pass1<D, RB, NW><<<a.Hq * a.S1, 64 * NW, 0, st>>>(a);
-  score_pass2<D, RB, NW><<<a.Hq * a.S2, 64 * NW, 0, st>>>(a);
+void launch_rb(const ScoreArgs& a, int w1, int w2, hipStream_t st) {
+  switch (w1) {
+    case 1: launch_pass1<D, RB, 1>(a, st); break;
+    case 2: launch_pass1<D, RB, 2>(a, st); break;
+    case 4: launch_pass1<D, RB, 4>(a, st); break;
+    default: launch_pass1<D, RB, 8>(a, st); break;
+  }
+  switch (w2) {
+    case 1: launch_pass2<D, RB, 1>(a, st); break;
+    case 2: launch_pass2<D, RB, 2>(a, st); break;
+    default: launch_pass2<D, RB, 4>(a, st); break;
+  }
 }
 
 template <int D>
-void launch_d(const ScoreArgs& a, int rb, hipStream_t st) {
+void launch_d(const ScoreArgs& a, int rb, int w1, int w2, hipStream_t st) {
   switch (rb) {
-    case 1: launch_passes<D, 1>(a, st); break;
-    case 2: launch_passes<D, 2>(a, st); break;
-    case 4: launch_passes<D, 4>(a, st); break;
-    case 6: launch_passes<D, 6>(a, st); break;
-    default: launch_passes<D, 8>(a, st); break;
+    case 1: launch_rb<D, 1>(a, w1, w2, st); break;
+    case 2: launch_rb<D, 2>(a, w1, w2, st); break;
+    case 4: launch_rb<D, 4>(a, w1, w2, st); break;
+    case 6: launch_rb<D, 6>(a, w1, w2, st); break;
+    default: launch_rb<D, 8>(a, w1, w2, st); break;
   }
 }
 
@@ -338,20 +517,42 @@ int pick_rb(int T) {
   return 8;
 }
 
-// splits so that Hq * S is about 2 workgroups per CU, each with >= 8 key blocks per wave
-int pick_splits(int Hq, int Hkv, int keys, int* kps, int* remap) {
-  const int target = 2 * num_cus();
-  int S = std::max(1, (target + Hq - 1) / Hq);
-  const int max_s = std::max(1, keys / (4 * 32 * 2));
-  S = std::min(S, max_s);
-  // make the (split, KV head) group count a multiple of 8 for the XCD placement
-  while ((S * Hkv) % 8 != 0 && S < 8 * max_s) ++S;
-  int per = (keys + S - 1) / S;
-  per = (per + 31) / 32 * 32;
-  S = (keys + per - 1) / per;
-  *kps = per;
-  *remap = ((S * Hkv) % 8 == 0) ? 1 : 0;
-  return S;
+// waves per workgroup: the q heads of a KV group, rounded up to a power of two,
+// at most `cap`.  Pass 1 takes up to 8 (two waves per SIMD hide each other's
+// waits); pass 2 up to 4 (it is bound by exp throughput, and one wave per SIMD
+// spares the barrier across eight)
+int pick_waves(int G, int cap) {
+  int w = 1;
+  while (w < G && w < cap) w *= 2;
+  return w;
+}
+
+// key splits so that there is about one workgroup per compute unit, with at
+// least 2 tiles per split; the split length is a whole number of tiles
+int pick_splits(int groups, int w, int keys, int* kps) {
+  (void)w;
+  const int target = std::max(1, num_cus());
+  int S = std::max(1, (target + groups - 1) / groups);
+  const int tiles = (keys + kTileKeys - 1) / kTileKeys;
+  S = std::max(1, std::min(S, tiles / 2));
+  const int per_tiles = (tiles + S - 1) / S;
+  *kps = per_tiles * kTileKeys;
+  return (keys + *kps - 1) / *kps;
+}
+
+struct Geometry {
+  int W1, HG1, S1, kps1, W2, HG2, S2, kps2;
+};
+Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+  Geometry gm;
+  const int G = Hq / Hkv;
+  gm.W1 = pick_waves(G, 8);
+  gm.HG1 = (G + gm.W1 - 1) / gm.W1;
+  gm.S1 = pick_splits(Hkv * gm.HG1, gm.W1, q_pos0 + T, &gm.kps1);
+  gm.W2 = pick_waves(G, 4);
+  gm.HG2 = (G + gm.W2 - 1) / gm.W2;
+  gm.S2 = pick_splits(Hkv * gm.HG2, gm.W2, n_vis, &gm.kps2);
+  return gm;
 }
 
 }  // namespace
@@ -361,9 +562,9 @@ using namespace svlm;
 
 extern "C" size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
   if (T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || q_pos0 < 0 || n_vis < 1) return 0;
-  int kps, remap;
-  const int S1 = pick_splits(Hq, Hkv, q_pos0 + T, &kps, &remap);
-  return (size_t)Hq * T * S1 * 2 * sizeof(float) + (size_t)Hq * n_vis * sizeof(float);
+  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
+  const size_t ml = ((size_t)Hq * T * gm.S1 * 2 * sizeof(float) + 255) / 256 * 256;
+  return ml + (size_t)Hkv * gm.HG2 * n_vis * sizeof(float);
 }
 
 extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const void* k, int64_t k_sh, int64_t k_sn,
@@ -403,25 +604,32 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
   a.G = Hq / Hkv;
   a.c = scale * kLog2e;
   // pass 1 covers keys [0, q_pos0 + T): everything any text row sees
-  a.S1 = pick_splits(Hq, Hkv, q_pos0 + T, &a.kps1, &a.remap1);
-  a.S2 = pick_splits(Hq, Hkv, n_vis, &a.kps2, &a.remap2);
-  if (a.S1 > 1024) return fail(SVLM_E_UNSUPPORTED, "svlm_score: too many key splits");
-  const size_t ml_bytes = (size_t)Hq * T * a.S1 * 2 * sizeof(float);
+  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
+  a.HG1 = gm.HG1;
+  a.HG2 = gm.HG2;
+  a.S1 = gm.S1;
+  a.kps1 = gm.kps1;
+  a.S2 = gm.S2;
+  a.kps2 = gm.kps2;
+  const size_t ml_bytes = ((size_t)Hq * T * a.S1 * 2 * sizeof(float) + 255) / 256 * 256;
   const size_t need = svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis);
   if (!ws || ws_bytes < need)
     return fail(SVLM_E_WORKSPACE, "svlm_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   if (!aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_score: workspace must be 16-byte aligned");
   a.ml = (float*)ws;
-  a.head = (float*)((char*)ws + ml_bytes);
+  a.grp = (float*)((char*)ws + ml_bytes);
   a.agg = agg;
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
   hipStream_t st = (hipStream_t)stream;
   const int rb = pick_rb(T);
-  if (D == 128) launch_d<128>(a, rb, st);
-  else launch_d<64>(a, rb, st);
-  const int rows = (agg == SVLM_AGG_QHEAD) ? Hq : (agg == SVLM_AGG_KVHEAD ? Hkv : 1);
-  score_agg<<<dim3((unsigned)((n_vis + 255) / 256), (unsigned)rows), 256, 0, st>>>(a);
+  if (D == 128) launch_d<128>(a, rb, gm.W1, gm.W2, st);
+  else launch_d<64>(a, rb, gm.W1, gm.W2, st);
+  const bool direct = (agg == SVLM_AGG_QHEAD) || (agg == SVLM_AGG_KVHEAD && gm.HG2 == 1);
+  if (!direct) {
+    const int rows = (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
+    score_agg<<<dim3((unsigned)((n_vis + 255) / 256), (unsigned)rows), 256, 0, st>>>(a);
+  }
   return check_launch("svlm_score");
 }

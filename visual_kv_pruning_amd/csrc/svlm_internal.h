@@ -70,6 +70,11 @@ __device__ __forceinline__ float fmax_nn(float a, float b) {
   __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ float fmax3_nn(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Cross-lane butterflies on the VALU (gfx950 v_permlane16/32_swap): after the
 // swap the two results hold the values of lanes l and l ^ 16 (or l ^ 32).
@@ -89,6 +94,98 @@ __device__ __forceinline__ float sum_xor16(float x) {
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
   return bits_f(r[0]) + bits_f(r[1]);
+}
+
+
+// ---------------------------------------------------------------------------
+// device side: buffer loads, LDS-DMA staging and their waits
+// ---------------------------------------------------------------------------
+// buffer descriptor word 3 for gfx9-family raw buffer loads (no swizzle, no stride)
+constexpr int kBufferFlags = 0x00020000;
+// cache policy of the streaming KV loads: nontemporal
+constexpr int kNT = 2;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int enc = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+  __builtin_amdgcn_s_waitcnt(enc);
+  __asm__ volatile("" ::: "memory");
+}
+
+// LDS reads of one staged key block, issued together and waited for inside
+// the same asm block, so no read is in flight when the outputs are used.  The
+// staging ring is written by LDS-DMA transfers whose completion the kernel
+// tracks with its own vmcnt waits; reads that the compiler cannot see keep it
+// from adding waits on every transfer in flight.  Outputs are early-clobber:
+// a read may complete while later reads of the block are still queued.
+__device__ __forceinline__ void lds_read_b128x8(u32x4 (&d)[8], const unsigned (&a)[8]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_b128x2(u32x4 (&d)[2], const unsigned (&a)[2]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1])
+      : "v"(a[0]), "v"(a[1])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_b128x4(u32x4 (&d)[4], const unsigned (&a)[4]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_b128x2_b64x4(u32x4 (&k)[2], u32x2 (&v)[4], const unsigned (&a)[6]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b64 %2, %8\n\t"
+      "ds_read_b64 %3, %9\n\t"
+      "ds_read_b64 %4, %10\n\t"
+      "ds_read_b64 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __asm__ volatile("" ::: "memory");
+}
+
+// Workgroup-wide execution barrier without a memory fence: LDS-DMA staging
+// slots are handed over by each wave's own vmcnt waits before it, so the
+// barrier must not drain the transfers still in flight (a fenced barrier
+// waits for every outstanding vector-memory operation).
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -9,11 +9,13 @@
 //
 // Exactness: masses are floor(s * 2^40) integers (exact for fp32 s in [0,1]),
 // sums are uint64, the target is ceil(double(Q) * P) in round-to-nearest
-// doubles; stage I is found by a 32-step bitwise descent over the fp32 key
-// bits with block-wide (count, mass) reductions - no atomics, so no
-// contention on nearly flat rows and no order dependence; stage II is a
-// per-token integer test on its rank in the remainder.  Ranks and output
-// positions come from ordered block scans, so `kept` is written ascending.
+// doubles.  The stage-I threshold key is found by a four-level radix descent
+// (8 bits of the fp32 key per level) over per-wave LDS histograms of integer
+// (count, mass), so the result does not depend on the order of the additions.
+// A thread owns a contiguous run of tokens; one ordered block scan of its
+// (above-threshold, tie) counts gives every token its stage-I rank, and the
+// stage-II picks before any remainder rank have a closed form, so `kept` is
+// written ascending without further scans.
 #pragma clang fp contract(off)
 
 #include <cmath>
@@ -25,13 +27,15 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 4;                     // elements per thread per scan chunk
-constexpr int kChunk = kThreads * kPer;
+constexpr int kRegKeys = 32;  // keys per thread held in registers (rows up to 32768 tokens)
+constexpr int kCopies = 32;
+constexpr int kCntStride = 257;   // words
+constexpr int kMassStride = 257;  // 8-byte words
 
 struct SelArgs {
   const float* scores;
   int64_t row_stride;
-  int N, budget, gh_gw;
+  int N, budget;
   double top_p;
   int32_t* kept;
   int32_t* n_stage1;
@@ -47,69 +51,89 @@ __device__ __forceinline__ uint64_t mass_of_key(unsigned key) {
   return (uint64_t)(bits_f(key) * 0x1p40f);  // exact: power-of-two scale, then floor
 }
 
-struct Red {
-  unsigned cnt;
-  uint64_t mass;
-};
-
-// block-wide sums; every thread gets the totals
-__device__ Red block_sum(Red r, Red* sm) {
+// wave-wide sum of a 64-bit value (every lane gets it)
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    r.cnt += __shfl_xor(r.cnt, off);
-    r.mass += __shfl_xor(r.mass, off);
-  }
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) sm[wv] = r;
-  __syncthreads();
-  Red t = {0u, 0ull};
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    t.cnt += sm[w].cnt;
-    t.mass += sm[w].mass;
-  }
-  return t;
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
-// block-wide exclusive scan of per-thread counts in thread order
-__device__ unsigned block_excl_scan(unsigned x, unsigned* total, unsigned* sm) {
+// block-wide exclusive scan (thread order) of two counters packed in 64 bits
+// (each part < 2^32; tokens per row < 2^18)
+__device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  unsigned incl = x;
+  uint64_t incl = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const unsigned y = __shfl_up(incl, off);
+    const uint64_t y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
-  __syncthreads();
   if (lane == 63) sm[wv] = incl;
   __syncthreads();
-  unsigned before = 0, tot = 0;
+  uint64_t before = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const unsigned v = sm[w];
-    if (w < wv) before += v;
-    tot += v;
-  }
-  *total = tot;
+  for (int w = 0; w < kWaves; ++w)
+    if (w < wv) before += sm[w];
   return before + incl - x;
 }
 
+// KREG > 0: the thread's run of keys lives in registers; KREG == 0: it is read
+// from memory on every pass
+template <int KREG>
 __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
-  __shared__ Red sm_red[kWaves];
-  __shared__ unsigned sm_scan[kWaves];
+  // kCopies histogram copies, lane l adding to copy l % kCopies, so that at
+  // most 64 / kCopies lanes of a wave meet on one counter (scores cluster in
+  // a few exponents, and a shared counter serialises every lane on it); the
+  // padded strides put one bin's copies in different banks
+  __shared__ unsigned h_cnt[kCopies * kCntStride];
+  __shared__ unsigned long long h_mass[kCopies * kMassStride];
+  __shared__ unsigned t_cnt[256];
+  __shared__ unsigned long long t_mass[256];
+  __shared__ unsigned long long sm_q[kWaves];
+  __shared__ uint64_t sm_scan[kWaves];
+  __shared__ unsigned sm_digit;
+  __shared__ unsigned sm_cnt_above;
+  __shared__ unsigned long long sm_mass_above;
+
   const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* s = a.scores + (int64_t)row * a.row_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float* srow = a.scores + (int64_t)row * a.row_stride;
   const int N = a.N, B = a.budget;
+  // this thread's run of tokens: [n_begin, n_begin + n_mine)
+  const int per = (N + kThreads - 1) / kThreads;
+  const int n_begin = min(N, tid * per);
+  const int n_mine = min(per, N - n_begin);
+
+  unsigned keys[KREG > 0 ? KREG : 1];
+  if constexpr (KREG > 0) {
+#pragma unroll
+    for (int e = 0; e < KREG; ++e) keys[e] = (e < n_mine) ? key_of(srow[n_begin + e]) : 0u;
+  }
+  auto key_at = [&](int e) -> unsigned {
+    if constexpr (KREG > 0) return keys[e];
+    else return key_of(srow[n_begin + e]);
+  };
 
   // ---- total fixed-point mass of the row
-  Red mine = {0u, 0ull};
-  for (int n = tid; n < N; n += kThreads) mine.mass += mass_of_key(key_of(s[n]));
-  const uint64_t Q = block_sum(mine, sm_red).mass;
+  uint64_t q = 0;
+  if constexpr (KREG > 0) {
+#pragma unroll
+    for (int e = 0; e < KREG; ++e)
+      if (e < n_mine) q += mass_of_key(keys[e]);
+  } else {
+    for (int n = tid; n < N; n += kThreads) q += mass_of_key(key_of(srow[n]));
+  }
+  q = wave_sum64(q);
+  if (lane == 0) sm_q[wv] = q;
+  __syncthreads();
+  uint64_t Q = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) Q += sm_q[w];
 
-  // ---- stage I: k1 = a_cnt + c taken, keys > vstar all taken, c ties at vstar by index
+  // ---- stage I: threshold key vstar; cnt_above / mass_above over keys > vstar
   unsigned vstar = 0xFFFFFFFFu;  // nothing taken when k1 == 0
+  unsigned cnt_above = 0;
+  uint64_t mass_above = 0;
   int k1 = 0, c_ties = 0;
   bool any_stage1 = (B > 0) && (a.top_p > 0.0);
   uint64_t Tm = ~0ull;
@@ -119,25 +143,103 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   }
   if (any_stage1) {
     unsigned prefix = 0;
-    unsigned cnt_above = 0;
-    uint64_t mass_above = 0;
-    for (int j = 31; j >= 0; --j) {
-      const unsigned cand = prefix | (1u << j);
-      Red r = {0u, 0ull};
-      for (int n = tid; n < N; n += kThreads) {
-        const unsigned key = key_of(s[n]);
-        if ((key >> j) == (cand >> j)) {
-          r.cnt += 1;
-          r.mass += mass_of_key(key);
+    for (int i = tid; i < kCopies * kCntStride; i += kThreads) {
+      h_cnt[i] = 0u;
+      h_mass[i] = 0ull;
+    }
+    __syncthreads();
+    unsigned* const my_cnt = h_cnt + (lane % kCopies) * kCntStride;
+    unsigned long long* const my_mass = h_mass + (lane % kCopies) * kMassStride;
+    for (int level = 0; level < 4; ++level) {
+      const int shift = 24 - 8 * level;
+      // keys under the current prefix, binned by their next 8 bits
+      auto bin_key = [&](unsigned key) {
+        asm volatile("" : "+v"(key));  // keeps the per-key masses from being hoisted out of the level loop
+        if (level == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
+          const unsigned bin = (key >> shift) & 255u;
+          atomicAdd(&my_cnt[bin], 1u);
+          atomicAdd(&my_mass[bin], (unsigned long long)mass_of_key(key));
+        }
+      };
+      if constexpr (KREG > 0) {
+#pragma unroll
+        for (int e = 0; e < KREG; ++e)
+          if (e < n_mine) bin_key(keys[e]);
+      } else {
+        for (int n = tid; n < N; n += kThreads) bin_key(key_of(srow[n]));
+      }
+      __syncthreads();
+      // one thread per bin adds up the copies and clears them for the next level
+      if (tid < 256) {
+        unsigned cc = 0;
+        uint64_t mm = 0;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+          cc += h_cnt[c * kCntStride + tid];
+          mm += h_mass[c * kMassStride + tid];
+          h_cnt[c * kCntStride + tid] = 0u;
+          h_mass[c * kMassStride + tid] = 0ull;
+        }
+        t_cnt[tid] = cc;
+        t_mass[tid] = mm;
+      }
+      __syncthreads();
+      // wave 0: the highest digit d whose bins d..255 (added to the keys
+      // above the prefix) reach the budget or the mass target
+      if (wv == 0) {
+        unsigned c4[4];
+        uint64_t m4[4];
+        unsigned ct = 0;
+        uint64_t mt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // lane holds bins 255 - 4 lane - i (top-down)
+          const int bin = 255 - 4 * lane - i;
+          c4[i] = t_cnt[bin];
+          m4[i] = t_mass[bin];
+          ct += c4[i];
+          mt += m4[i];
+        }
+        // inclusive prefix over lanes, then the part above this lane's bins
+        uint64_t ci = ct, mi = mt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint64_t yc = __shfl_up(ci, off);
+          const uint64_t ym = __shfl_up(mi, off);
+          if (lane >= off) {
+            ci += yc;
+            mi += ym;
+          }
+        }
+        uint64_t cb = ci - ct, mb = mi - mt;
+        int found = -1;
+        uint64_t c_above_d = 0, m_above_d = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t c_incl = cb + c4[i], m_incl = mb + m4[i];
+          if (found < 0 && (cnt_above + c_incl >= (uint64_t)B || mass_above + m_incl >= Tm)) {
+            found = i;
+            c_above_d = cb;
+            m_above_d = mb;
+          }
+          cb = c_incl;
+          mb = m_incl;
+        }
+        // some bin always qualifies: all N >= B keys lie under the prefix at
+        // level 0, and the chosen bin qualifies again one level down
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(found >= 0);
+        const int first = (hit != 0ull) ? (int)__builtin_ctzll(hit) : 63;
+        if (lane == first) {
+          sm_digit = (unsigned)(255 - 4 * lane - (found >= 0 ? found : 3));
+          sm_cnt_above = cnt_above + (unsigned)c_above_d;
+          sm_mass_above = mass_above + m_above_d;
         }
       }
-      r = block_sum(r, sm_red);
-      if (cnt_above + r.cnt >= (unsigned)B || mass_above + r.mass >= Tm) {
-        prefix = cand;
-      } else {
-        cnt_above += r.cnt;
-        mass_above += r.mass;
-      }
+      __syncthreads();
+      // read before the next level's wave-0 step rewrites them, which is two
+      // barriers away
+      prefix |= sm_digit << shift;
+      cnt_above = sm_cnt_above;
+      mass_above = sm_mass_above;
     }
     vstar = prefix;
     int c = B - (int)cnt_above;
@@ -152,83 +254,95 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
     k1 = (int)cnt_above + c;
   }
 
-  // ---- stage II parameters
-  const int64_t n_rem = N - k1;
-  const int64_t m_fill = B - k1;
-
-  // ---- ordered pass: ties -> stage-I flags -> remainder ranks -> stage-II flags -> positions
-  unsigned tie_carry = 0, s1_carry = 0, kept_carry = 0;
-  for (int base = 0; base < N; base += kChunk) {
-    const int n0 = base + tid * kPer;
-    unsigned key[kPer];
-    unsigned tie_cnt = 0;
+  // ---- stage-I ranks: one ordered scan of (keys above vstar, ties at vstar)
+  unsigned my_above = 0, my_ties = 0;
+  if (k1 > 0) {
+    if constexpr (KREG > 0) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      key[e] = (n0 + e < N) ? key_of(s[n0 + e]) : 0u;
-      tie_cnt += (n0 + e < N && k1 > 0 && key[e] == vstar) ? 1u : 0u;
-    }
-    unsigned tot;
-    unsigned tie_before = tie_carry + block_excl_scan(tie_cnt, &tot, sm_scan);
-    tie_carry += tot;
-
-    bool s1[kPer];
-    unsigned s1_cnt = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      bool f = false;
-      if (n0 + e < N && k1 > 0) {
-        if (key[e] > vstar) f = true;
-        else if (key[e] == vstar) {
-          f = tie_before < (unsigned)c_ties;
-          ++tie_before;
+      for (int e = 0; e < KREG; ++e)
+        if (e < n_mine) {
+          my_above += keys[e] > vstar ? 1u : 0u;
+          my_ties += keys[e] == vstar ? 1u : 0u;
         }
+    } else {
+      for (int e = 0; e < n_mine; ++e) {
+        const unsigned key = key_at(e);
+        my_above += key > vstar ? 1u : 0u;
+        my_ties += key == vstar ? 1u : 0u;
       }
-      s1[e] = f;
-      s1_cnt += f ? 1u : 0u;
     }
-    unsigned s1_before = s1_carry + block_excl_scan(s1_cnt, &tot, sm_scan);
-    s1_carry += tot;
+  }
+  const uint64_t before = block_excl_scan64(((uint64_t)my_ties << 32) | my_above, sm_scan);
+  const unsigned above_before = (unsigned)before;
+  unsigned ties_before = (unsigned)(before >> 32);
 
-    bool kp[kPer];
-    uint8_t tg[kPer];
-    unsigned kept_cnt = 0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int n = n0 + e;
-      bool k = false;
-      uint8_t t = 0;
-      if (n < N) {
-        if (s1[e]) {
-          k = true;
-          t = 1;
-          ++s1_before;
-        } else if (m_fill > 0) {
-          const int64_t rho = (int64_t)n - s1_before;   // rank among the remainder
-          const int64_t num = 2 * m_fill * rho - n_rem;
-          const int64_t den = 2 * n_rem;
-          int64_t j = (num <= 0) ? 0 : (num + den - 1) / den;
-          if (j < m_fill && ((2 * j + 1) * n_rem) / (2 * m_fill) == rho) {
-            k = true;
-            t = 2;
+  // ---- flags and output positions, token by token in raster order.  Stage-I
+  // tokens before n: above_before + min(c_ties, ties_before).  A remainder
+  // token's rank is rho = n - that; stage II keeps the ranks
+  // floor((2j+1) n_rem / (2m)), j < m, and the picks at ranks below rho number
+  // min(m, ceil((2 m rho - n_rem) / (2 n_rem))).  The thread finds its first
+  // pending pick with one division and steps to the next ones by adding
+  // n_rem / m with a carried remainder.
+  const int n_rem = N - k1;
+  const int m_fill = B - k1;
+  const unsigned two_m = 2u * (unsigned)max(m_fill, 1);
+  unsigned s1_before = above_before + min(ties_before, (unsigned)c_ties);
+  int rho = n_begin - (int)s1_before;
+  int pb = 0;              // stage-II picks at ranks below rho
+  unsigned next_q = ~0u;   // rank of pick pb (none when pb == m)
+  unsigned next_r = 0;     // (2 pb + 1) n_rem mod 2m
+  const unsigned step_q = (unsigned)(2 * n_rem) / two_m, step_r = (unsigned)(2 * n_rem) % two_m;
+  if (m_fill > 0) {
+    const int64_t num = 2 * (int64_t)m_fill * rho - n_rem;
+    int64_t j = (num <= 0) ? 0 : (num + 2 * (int64_t)n_rem - 1) / (2 * (int64_t)n_rem);
+    pb = (int)(j < m_fill ? j : m_fill);
+    if (pb < m_fill) {
+      const uint64_t t = (uint64_t)(2 * pb + 1) * (uint64_t)n_rem;
+      next_q = (unsigned)(t / two_m);
+      next_r = (unsigned)(t % two_m);
+    }
+  }
+  int32_t* const kept_row = a.kept + (int64_t)row * B;
+  uint8_t* const tag_row = a.tag ? a.tag + (int64_t)row * N : nullptr;
+  auto emit = [&](int e, unsigned key) {
+    const int n = n_begin + e;
+    const bool is_above = (k1 > 0) && key > vstar;
+    const bool is_tie = (k1 > 0) && key == vstar;
+    const bool s1 = is_above || (is_tie && ties_before < (unsigned)c_ties);
+    uint8_t tg = 0;
+    if (s1) {
+      tg = 1;
+      kept_row[s1_before + pb] = n;
+    } else {
+      if ((unsigned)rho == next_q) {
+        tg = 2;
+        kept_row[s1_before + pb] = n;
+        ++pb;
+        if (pb < m_fill) {
+          next_q += step_q;
+          next_r += step_r;
+          if (next_r >= two_m) {
+            next_r -= two_m;
+            ++next_q;
           }
+        } else {
+          next_q = ~0u;
         }
       }
-      kp[e] = k;
-      tg[e] = t;
-      kept_cnt += k ? 1u : 0u;
     }
-    unsigned pos = kept_carry + block_excl_scan(kept_cnt, &tot, sm_scan);
-    kept_carry += tot;
+    // counters advance arithmetically (a branch on which one to bump makes the
+    // compiler address them through memory)
+    s1_before += s1 ? 1u : 0u;
+    rho += s1 ? 0 : 1;
+    if (tag_row) tag_row[n] = tg;
+    ties_before += is_tie ? 1u : 0u;
+  };
+  if constexpr (KREG > 0) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int n = n0 + e;
-      if (n >= N) continue;
-      if (kp[e]) {
-        if (pos < (unsigned)B) a.kept[(int64_t)row * B + pos] = n;
-        ++pos;
-      }
-      if (a.tag) a.tag[(int64_t)row * N + n] = tg[e];
-    }
+    for (int e = 0; e < KREG; ++e)
+      if (e < n_mine) emit(e, keys[e]);
+  } else {
+    for (int e = 0; e < n_mine; ++e) emit(e, key_at(e));
   }
   if (tid == 0) a.n_stage1[row] = k1;
 }
@@ -262,11 +376,11 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   a.row_stride = row_stride;
   a.N = (int)N;
   a.budget = budget;
-  a.gh_gw = H * W;
   a.top_p = top_p;
   a.kept = kept;
   a.n_stage1 = n_stage1;
   a.tag = tag;
-  select_rows<<<R, kThreads, 0, (hipStream_t)stream>>>(a);
+  if (N <= (int64_t)kThreads * kRegKeys) select_rows<kRegKeys><<<R, kThreads, 0, (hipStream_t)stream>>>(a);
+  else select_rows<0><<<R, kThreads, 0, (hipStream_t)stream>>>(a);
   return check_launch("svlm_select");
 }

@@ -411,13 +411,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   }
 }
 
-// Separate merge launch for large partial volumes: kCombineRows rows per
-// workgroup, 128 threads per row = D/4 column groups x (512/D) split parts.
-// Every thread issues all loads of its splits at once (one memory round trip),
-// merges them against its own running maximum, and the parts are combined in
-// a fixed order through LDS.  Deterministic.
+// Merge launch: kCombineRows rows per workgroup, 128 threads per row = D/4
+// column groups x (512/D) split parts.  With at most SPAN splits per part, a
+// thread loads all of its (max, sum, output) partials at once — one memory
+// round trip — and merges them in split order; SPAN = 0 loops over any number.
+// The parts are then combined in a fixed order through LDS.  Deterministic.
 constexpr int kCombineRows = 2;
-template <int D>
+constexpr int kCombineSpan = 8;
+template <int D, int SPAN>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   constexpr int C4 = D / 4;
   constexpr int PARTS = 128 / C4;
@@ -435,18 +436,42 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (R < rows_total) {
     const float2* ml = (const float2*)a.ws_ml + R * S;
     const float4* po = (const float4*)(a.ws_o + R * S * D) + d4;
-    for (int sp = s_lo; sp < s_hi; ++sp) M = fmaxf(M, ml[sp].x);
-    if (M != kNegInf) {
+    if constexpr (SPAN > 0) {
+      float2 st[SPAN];
+      float4 v[SPAN];
+#pragma unroll
+      for (int i = 0; i < SPAN; ++i) {
+        const int sp = s_lo + i;
+        st[i] = (sp < s_hi) ? ml[sp] : make_float2(kNegInf, 0.f);
+        v[i] = (sp < s_hi) ? po[(int64_t)sp * C4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < SPAN; ++i) M = fmaxf(M, st[i].x);
+      if (M != kNegInf) {
+#pragma unroll
+        for (int i = 0; i < SPAN; ++i) {
+          const float w = (st[i].x == kNegInf) ? 0.f : exp2f(st[i].x - M);
+          L += w * st[i].y;
+          acc.x += w * v[i].x;
+          acc.y += w * v[i].y;
+          acc.z += w * v[i].z;
+          acc.w += w * v[i].w;
+        }
+      }
+    } else {
+      for (int sp = s_lo; sp < s_hi; ++sp) M = fmaxf(M, ml[sp].x);
+      if (M != kNegInf) {
 #pragma unroll 8
-      for (int sp = s_lo; sp < s_hi; ++sp) {
-        const float2 st = ml[sp];
-        const float4 v = po[(int64_t)sp * C4];
-        const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
-        L += w * st.y;
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+        for (int sp = s_lo; sp < s_hi; ++sp) {
+          const float2 st = ml[sp];
+          const float4 v = po[(int64_t)sp * C4];
+          const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
+          L += w * st.y;
+          acc.x += w * v.x;
+          acc.y += w * v.y;
+          acc.z += w * v.z;
+          acc.w += w * v.w;
+        }
       }
     }
   }
@@ -478,6 +503,14 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
   *(float4*)(a.out + orow * D + 4 * d4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   if (a.lse && d4 == 0) a.lse[orow] = (Lt > 0.f) ? (Mt + log2f(Lt)) * kLn2 : kNegInf;
+}
+
+template <int D>
+void launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
+  constexpr int PARTS = 128 / (D / 4);
+  const unsigned blocks = (unsigned)(((int64_t)batch * a.Hkv * a.rows + kCombineRows - 1) / kCombineRows);
+  if ((a.splits + PARTS - 1) / PARTS <= kCombineSpan) attn_combine<D, kCombineSpan><<<blocks, 256, 0, st>>>(a);
+  else attn_combine<D, 0><<<blocks, 256, 0, st>>>(a);
 }
 
 template <int D, int RB>
@@ -614,9 +647,8 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   if (D == 128) launch_d<128>(a, p.rb, batch, p.row_chunks, st);
   else launch_d<64>(a, p.rb, batch, p.row_chunks, st);
   if (p.splits > 1) {
-    const unsigned blocks = (unsigned)(((int64_t)batch * Hkv * a.rows + kCombineRows - 1) / kCombineRows);
-    if (D == 128) attn_combine<128><<<blocks, 256, 0, st>>>(a);
-    else attn_combine<64><<<blocks, 256, 0, st>>>(a);
+    if (D == 128) launch_combine<128>(a, batch, st);
+    else launch_combine<64>(a, batch, st);
   }
   return check_launch("svlm_decode_attn");
 }

@@ -1,5 +1,7 @@
 """Mean text->visual attention on the GPU vs the fp64 oracle: within 1e-5 absolute
 (and the relative error on scores >= 1e-6 reported)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -89,3 +91,24 @@ def test_deterministic():
     a = _gpu_score(p, cfg, "qhead")
     b = _gpu_score(p, cfg, "qhead")
     assert np.array_equal(a, b)
+
+
+def test_deterministic_full_layer():
+    """Repeated calls on a full 72B-shape layer give bit-identical rows (every
+    pass-1 reference maximum and every merge is order-fixed)."""
+    cfg = W.C3
+    p = W.prefill_layer(cfg, 0)
+    log("score case 72B layer, repeated calls")
+    first = _gpu_score(p, cfg, "all")
+    for _ in range(3):
+        assert np.array_equal(first, _gpu_score(p, cfg, "all"))
+
+
+def test_wide_score_range():
+    """Queries scaled by 4 (exactly, in bf16) spread the scores over ~25 log2
+    units, so the per-lane reference maximum of pass 1 is raised many times."""
+    cfg = W.C2
+    p = W.prefill_layer(cfg, 0)
+    p = dataclasses.replace(p, q_text=p.q_text * 4.0)
+    log("score case wide score range")
+    _compare(_gpu_score(p, cfg, "kvhead"), _ref(p, cfg, "kvhead"), "C2 q x4")

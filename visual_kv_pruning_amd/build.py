@@ -25,6 +25,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# per-source additions: the score passes keep their matrix-core accumulators in
+# ordinary VGPRs (the exponentials read every one of them; accumulator
+# registers would cost a move per element)
+EXTRA = {
+    "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -33,7 +39,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")

@@ -31,7 +31,7 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 constexpr int kTileKeys = 64;      // keys per staged K tile
-constexpr float kRescale = 8.f;    // log2 headroom before a row's reference maximum is raised
+constexpr float kRescaleSum = 256.f;  // a lane's 4-key weight sum above this raises its reference maximum
 constexpr int kLseBatch = 16;      // pass-1 partials loaded at once when a row's log-sum-exp is formed
 
 struct ScoreArgs {
@@ -170,6 +170,28 @@ __device__ __forceinline__ void colsum_half(const f32x4 (&S)[RB][2], const float
     }
 }
 
+// the lane's part of the column sum of P = exp2(c s - lse) for one 16-key
+// block (lane: rows 16 rb + 4 g4 + i, key c).  One block at a time keeps the
+// score accumulators few enough to live in ordinary VGPRs next to the query
+// registers, so the exponentials read them without accumulator moves.
+template <int RB, int KK>
+__device__ __forceinline__ float qk_colsum_block(const u32x4 (&q)[RB][KK], const u32x4 (&kq)[KK],
+                                                 const float (&lse)[RB][4], float c) {
+  f32x4 S[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) S[rb] = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[kk]), S[rb]);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += fast_exp2(fmaf(S[rb][i], c, -lse[rb][i]));
+  return acc;
+}
+
 // the 2 * KK K-operand chunks of key blocks kb0, kb0 + 1 of a staged tile
 template <int KK, int BLOCK_BYTES>
 __device__ __forceinline__ void read_k_pair(unsigned base, const unsigned (&ko)[KK], u32x4 (&kq)[2][KK]) {
@@ -279,17 +301,27 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = s0[e];
         }
-        const float lmax = fmax_nn(fmax3_nn(x[0], x[1], x[2]), x[3]) * a.c;
-        if (lmax > mc[rb] + kRescale) {  // per lane; after the first block only when a row's max jumps
-          const float m_new = fmax_nn(mc[rb], lmax);
-          l[rb] *= (mc[rb] == kNegInf) ? 0.f : fast_exp2(mc[rb] - m_new);
-          mc[rb] = m_new;
-        }
-        const float mneg = (mc[rb] == kNegInf) ? 0.f : -mc[rb];
+        // weights against the current reference: the 4-key sum exceeds
+        // kRescaleSum = 2^8 (or is inf / NaN: no reference yet) only when a
+        // score passes the reference by about 8 (log2 units); the reference is
+        // then raised to the block maximum and the weights recomputed.  The
+        // maximum is taken only on that rare path, so the hot path is one
+        // fma, one exp2 and one add per score.
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
-        l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, -mc[rb]));
+        float s4 = (p[0] + p[1]) + (p[2] + p[3]);
+        if (!(s4 <= kRescaleSum)) {
+          const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * a.c;
+          const float m_new = fmaxf(mc[rb], lmax);
+          l[rb] *= (mc[rb] == kNegInf) ? 0.f : fast_exp2(mc[rb] - m_new);
+          mc[rb] = m_new;
+          const float mneg = (m_new == kNegInf) ? 0.f : -m_new;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
+          s4 = (p[0] + p[1]) + (p[2] + p[3]);
+        }
+        l[rb] += s4;
       }
     }
   };
@@ -420,12 +452,10 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
     const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
     float col[4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4 kq[2][KK];
-      read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(hf * 32 * Ring::ROWB), ko, kq);
-      f32x4 S[RB][2];
-      qk_half<RB, KK>(qreg, kq, S);
-      colsum_half<RB>(S, lse, a.c, col[2 * hf], col[2 * hf + 1]);
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4 kq[KK];
+      read_k_block<KK>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq);
+      col[kb] = qk_colsum_block<RB, KK>(qreg, kq, lse, a.c);
     }
     // column sums over the rows held by the four lane groups; lane (c, g4) then
     // keeps key 16 g4 + c of the tile

@@ -172,3 +172,15 @@ def test_hour_long_shape_verify_sampled_heads():
     ro, rl = oracle.decode_attn(q[:, :, :G], k[:1], v[:1], [N], True)
     assert row_rel_err(o[:, :, :G], ro) <= TOL
     assert np.abs(lse[:, :, :G] - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("scale_q", [8.0, 32.0])
+def test_wide_score_range(scale_q):
+    """Queries scaled by a power of two (exact in bf16) spread the scores over
+    tens to hundreds of log2 units, so every row's reference maximum is raised
+    many times along the key loop, in split kernels and across splits."""
+    q = _rand(61, 1, 6, 16, 128) * scale_q
+    k = _rand(62, 2, 3000, 128)
+    v = _rand(63, 2, 3000, 128)
+    for splits in (1, 7):
+        _check(q, k, v, [3000], True, num_splits=splits, name=f"wide range q x{scale_q:g} splits {splits}")

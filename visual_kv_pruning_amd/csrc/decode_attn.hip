@@ -60,7 +60,7 @@ constexpr int kStep = kWaves * kBlock;     // keys per workgroup step
 constexpr int kMaxRB128 = 3;               // query row blocks per workgroup at D = 128 (48 rows)
 constexpr int kMaxRB64 = 5;                // 80 rows at D = 64
 constexpr float kNegInf = -INFINITY;
-constexpr float kRescale = 8.f;  // log2 headroom before the running maximum is raised
+constexpr float kRescaleSum = 256.f;  // a lane's 4-key weight sum above this raises the row references
 
 template <int DV>
 struct VRaw;
@@ -206,9 +206,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   const unsigned ring0 = lds_addr(my_ring);
 
   // Running state per row (lane row c + 16 rb, uniform over the four lane
-  // groups): m_use is the reference maximum in log2 units, raised only when a
-  // block's maximum exceeds it by more than kRescale, so the weights stay
-  // <= 2^kRescale and the fp32 accumulators are rescaled only rarely.
+  // groups): m_use is the reference maximum in log2 units, raised only when
+  // some lane's 4-key weight sum passes kRescaleSum, so single weights stay
+  // <= 2^8 and the fp32 accumulators are rescaled only rarely.
   float m_use[RB], l_run[RB];
   f32x4 o[DV][RB];
 #pragma unroll
@@ -267,28 +267,39 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), sacc[rb]);
 
-    float x[RB][4], mx[RB];
+    // weights against each row's reference.  A lane's 4-key sum exceeds
+    // kRescaleSum (or is inf / NaN: no reference yet) only when one of its
+    // scores passes the reference by about 6 (log2 units); then, for the whole
+    // wave, every row's reference is raised to its block maximum, the
+    // accumulators are rescaled and the weights recomputed.  Row maxima are
+    // taken only on that rare path.
+    float x[RB][4], p[RB][4], s4[RB];
+    bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[rb][i] = (!masked || key0 + 4 * g4 + i < lim[rb]) ? sacc[rb][i] : kNegInf;
+        p[rb][i] = fast_exp2(fmaf(x[rb][i], a.c, -m_use[rb]));
       }
-      const float m = fmax_nn(fmax_nn(x[rb][0], x[rb][1]), fmax_nn(x[rb][2], x[rb][3]));
-      mx[rb] = max_xor32(max_xor16(m)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
+      s4[rb] = (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
+      grow |= !(s4[rb] <= kRescaleSum);
     }
-    bool grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) grow |= (mx[rb] > m_use[rb] + kRescale);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = fmax_nn(m_use[rb], mx[rb]);
+        const float m = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
+        const float mx = max_xor32(max_xor16(m)) * a.c;  // raw scores -> log2 units (c > 0 keeps the order)
+        const float m_new = fmaxf(m_use[rb], mx);
         const float alpha = (m_use[rb] == kNegInf) ? 0.f : fast_exp2(m_use[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
         for (int mb = 0; mb < DV; ++mb) o[mb][rb] *= alpha;
         m_use[rb] = m_new;
+        const float mneg = (m_new == kNegInf) ? 0.f : -m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[rb][i] = fast_exp2(fmaf(x[rb][i], a.c, mneg));
+        s4[rb] = (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
       }
     }
     // P^T as the B operand of the 16x16x16 product: lane (c, g4) holds
@@ -296,18 +307,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
     bf16x4 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float mneg = (m_use[rb] == kNegInf) ? 0.f : -m_use[rb];
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(x[rb][i], a.c, mneg));
-      l_run[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+      l_run[rb] += s4[rb];
       u32x2 hi, lo;
 #pragma unroll
       for (int qd = 0; qd < 2; ++qd) {
-        const unsigned b0 = f_bits(p[2 * qd]), b1 = f_bits(p[2 * qd + 1]);
+        const unsigned b0 = f_bits(p[rb][2 * qd]), b1 = f_bits(p[rb][2 * qd + 1]);
         hi[qd] = perm(b1, b0, kPermHi);
-        const float r0 = p[2 * qd] - bits_f(b0 & 0xFFFF0000u);
-        const float r1 = p[2 * qd + 1] - bits_f(b1 & 0xFFFF0000u);
+        const float r0 = p[rb][2 * qd] - bits_f(b0 & 0xFFFF0000u);
+        const float r1 = p[rb][2 * qd + 1] - bits_f(b1 & 0xFFFF0000u);
         lo[qd] = perm(f_bits(r1), f_bits(r0), kPermHi);
       }
       phi[rb] = as_bf16x4(hi);

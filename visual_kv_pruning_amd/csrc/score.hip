@@ -184,12 +184,20 @@ __device__ __forceinline__ float qk_colsum_block(const u32x4 (&q)[RB][KK], const
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) S[rb] = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[kk]), S[rb]);
   }
-  float acc = 0.f;
+  // pairwise sums (a fixed tree, not one serial chain of RB * 4 dependent adds)
+  float r[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < RB; ++rb) {
+    float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc += fast_exp2(fmaf(S[rb][i], c, -lse[rb][i]));
-  return acc;
+    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(S[rb][i], c, -lse[rb][i]));
+    r[rb] = (e[0] + e[1]) + (e[2] + e[3]);
+  }
+#pragma unroll
+  for (int w = 1; w < RB; w *= 2)
+#pragma unroll
+    for (int rb = 0; rb + w < RB; rb += 2 * w) r[rb] += r[rb + w];
+  return r[0];
 }
 
 // the 2 * KK K-operand chunks of key blocks kb0, kb0 + 1 of a staged tile

@@ -103,11 +103,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   const int c = lane & 15;
   const int g4 = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int s = bid % a.splits;
-  bid /= a.splits;
-  const int h = bid % a.Hkv;
-  const int b = bid / a.Hkv;
+  // block id -> (batch, KV head) pair fastest, then split: workgroups go to
+  // the eight XCDs round-robin by id, so with 8 (or 4, 2) pairs every split of
+  // one pair runs on one XCD, which shares its queries through that XCD's L2
+  // and leaves the partials there for the merge launch (mapped the same way)
+  const int pairs = a.batch * a.Hkv;
+  const int ph = blockIdx.x % pairs;
+  const int s = blockIdx.x / pairs;
+  const int h = ph % a.Hkv;
+  const int b = ph / a.Hkv;
   const int row_base = blockIdx.y * RP;
 
   const int n_kv = min(max(a.kv_len[b], 0), a.max_kv_len);
@@ -433,15 +437,19 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   __shared__ float4 s_acc[256];
   __shared__ float2 s_ml[256];
   const int t = threadIdx.x;
-  const int64_t R = (int64_t)blockIdx.x * kCombineRows + t / 128;  // (b * Hkv + h) * rows + r
-  const int64_t rows_total = (int64_t)a.batch * a.Hkv * a.rows;
+  // block id -> (batch, KV head) pair fastest, as in the split kernel, then
+  // kCombineRows rows of that pair
+  const int pairs = a.batch * a.Hkv;
+  const int r_in = (int)(blockIdx.x / pairs) * kCombineRows + t / 128;
+  const bool valid = r_in < a.rows;
+  const int64_t R = (int64_t)(blockIdx.x % pairs) * a.rows + r_in;  // (b * Hkv + h) * rows + r
   const int d4 = (t & 127) % C4, part = (t & 127) / C4;
   const int S = a.splits;
   const int span = (S + PARTS - 1) / PARTS;
   const int s_lo = min(S, part * span), s_hi = min(S, s_lo + span);
   float M = kNegInf, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (R < rows_total) {
+  if (valid) {
     const float2* ml = (const float2*)a.ws_ml + R * S;
     const float4* po = (const float4*)(a.ws_o + R * S * D) + d4;
     if constexpr (SPAN > 0) {
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   s_acc[t] = acc;
   s_ml[t] = make_float2(M, L);
   __syncthreads();
-  if (R >= rows_total || part != 0) return;
+  if (!valid || part != 0) return;
   float Mt = kNegInf;
   for (int p = 0; p < PARTS; ++p) Mt = fmaxf(Mt, s_ml[t + p * C4].x);
   float Lt = 0.f;
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 template <int D>
 void launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
   constexpr int PARTS = 128 / (D / 4);
-  const unsigned blocks = (unsigned)(((int64_t)batch * a.Hkv * a.rows + kCombineRows - 1) / kCombineRows);
+  const unsigned blocks = (unsigned)((int64_t)batch * a.Hkv * ((a.rows + kCombineRows - 1) / kCombineRows));
   if ((a.splits + PARTS - 1) / PARTS <= kCombineSpan) attn_combine<D, kCombineSpan><<<blocks, 256, 0, st>>>(a);
   else attn_combine<D, 0><<<blocks, 256, 0, st>>>(a);
 }

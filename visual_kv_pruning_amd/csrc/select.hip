@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   unsigned keys[KREG > 0 ? KREG : 1];
   if constexpr (KREG > 0) {
 #pragma unroll
-    for (int e = 0; e < KREG; ++e) keys[e] = (e < n_mine) ? key_of(srow[n_begin + e]) : 0u;
+    for (int e = 0; e < KREG; ++e) keys[e] = key_of(srow[min(n_begin + e, N - 1)]);  // loads first, unconditional
+#pragma unroll
+    for (int e = 0; e < KREG; ++e) keys[e] = (e < n_mine) ? keys[e] : 0u;
   }
   auto key_at = [&](int e) -> unsigned {
     if constexpr (KREG > 0) return keys[e];

@@ -126,6 +126,11 @@ def main():
     ws_score = torch.empty(ops.score_workspace_bytes(T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, nqv, Hq, Hkv, D, N_full)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)), dtype=torch.uint8, device=dev)
+    ws_di = torch.empty(max(256, ops.decode_attn_indexed_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)),
+                        dtype=torch.uint8, device=dev)
+    # the draft's key list for the in-place variant: kept visual rows, then the text and newest rows
+    draft_idx = torch.empty(N_draft, dtype=torch.int32, device=dev)
+    draft_idx[B_keep:] = torch.arange(NV, NV + T + 1, dtype=torch.int32, device=dev)
     ws_acc = torch.empty(ops.verify_workspace_bytes(1, gv, V), dtype=torch.uint8, device=dev)
     o_v = torch.empty(1, nqv, Hq, D, dtype=torch.float32, device=dev)
     l_v = torch.empty(1, nqv, Hq, dtype=torch.float32, device=dev)
@@ -146,12 +151,16 @@ def main():
 
     def k_select():
         kept_box["kept"] = ops.select(row, cfg.frames, cfg.gh, cfg.gw, cfg.top_p, B_keep)[0]
+        draft_idx[:B_keep].copy_(kept_box["kept"][0])
 
     def k_gather(l):
         ops.gather_kv(K[l], Vv[l], kept_box["kept"][0], NV, T, draft_kv[0, l, :, :B_keep + T], draft_kv[1, l, :, :B_keep + T])
 
     def k_draft(l):
         ops.decode_attn(qd[l], draft_kv[0, l], draft_kv[1, l], kv_len_d, False, out=o_d, lse=l_d, ws=ws_d)
+
+    def k_draft_idx(l):
+        ops.decode_attn_indexed(qd[l], K[l], Vv[l], draft_idx, kv_len_d, False, out=o_d, lse=l_d, ws=ws_di)
 
     def k_verify_attn(l):
         ops.decode_attn(qv[l], K[l], Vv[l], kv_len_v, True, out=o_v, lse=l_v, ws=ws_v)
@@ -164,10 +173,12 @@ def main():
         "select": k_select,
         "gather": lambda: [k_gather(l) for l in range(L)],
         "draft_attn": lambda: [k_draft(l) for l in range(L)],
+        "draft_attn_indexed": lambda: [k_draft_idx(l) for l in range(L)],
         "verify_attn": lambda: [k_verify_attn(l) for l in range(L)],
         "accept": k_accept,
     }
-    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "verify_attn": L, "accept": 1}
+    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "draft_attn_indexed": L, "verify_attn": L,
+             "accept": 1}
 
     # warm up eagerly (also fills the library's device-property cache), then capture
     # each kernel sequence as a HIP graph so host launch overhead is out of the timings
@@ -183,8 +194,12 @@ def main():
         graphs[kind] = gr
     torch.cuda.synchronize()
 
+    # one step of the path: every kind but the in-place draft, which is the
+    # alternative to gather + compact draft and is timed on its own below
+    step_kinds = [k for k in seqs if k != "draft_attn_indexed"]
+
     def step():
-        for kind in seqs:
+        for kind in step_kinds:
             graphs[kind].replay()
 
     for _ in range(args.warmup):
@@ -244,6 +259,9 @@ def main():
     }
     kernels["verify_attn"].update(bytes=verify_bytes, gbs=round(verify_gbs, 1))
     kernels["draft_attn"].update(bytes=draft_bytes, gbs=round(draft_gbs, 1))
+    kernels["draft_attn_indexed"].update(
+        bytes=draft_bytes, gbs=round(draft_bytes / (per_us["draft_attn_indexed"] * 1e-6) / 1e9, 1),
+        what="the same draft read in place from the full cache through the key list (no gather)")
     kernels["score"].update(flop=score_flop, tflops=round(score_flop / (us_score * 1e-6) / 1e12, 1))
     kernels["gather"].update(bytes=2 * 2 * (B_keep + T) * Hkv * D * 2,
                              gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (per_us["gather"] * 1e-6) / 1e9, 1))

@@ -194,6 +194,34 @@ int svlm_decode_attn(const void* q, int64_t q_sb,
                      int num_splits, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * svlm_decode_attn_indexed - svlm_decode_attn over keys named by an index
+ * list, read in place from the full cache (the gather fused into the draft).
+ * [StD-sel] ("dual-module architecture": the sparse draft reads only the
+ * selected KV, per layer and head); [StD-dec].
+ *
+ * Key position n < n_idx[b] of batch b and KV head g is cache row
+ *   r = kv_idx[b * idx_sb + g * idx_sh + n]
+ * of k, v: [B][Hkv][kv_rows][D] bf16 with strides kv_sb, kv_sh, kv_sn.
+ * idx_sh = 0: one list for all heads; idx_sb = 0: one list for all batch
+ * entries.  The attention is svlm_decode_attn's with k[b,g,n] replaced by
+ * row r, and kv_len by n_idx (device int32 [B], precondition
+ * nq <= n_idx[b] <= max_n_idx; causal_tail applies to the last nq list
+ * positions).  Indices are a precondition in [0, kv_rows); one outside
+ * reads a zero row (the result is then undefined) and never reads memory
+ * outside the cache.  Requires kv_rows * kv_sn * 2 < 2^31.
+ * ws: svlm_decode_attn_indexed_workspace(...) bytes, same rules as above.
+ * ------------------------------------------------------------------------ */
+size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_n_idx,
+                                          int num_splits);
+int svlm_decode_attn_indexed(const void* q, int64_t q_sb,
+                             const void* k, const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                             int kv_rows, const int32_t* kv_idx, int64_t idx_sb, int64_t idx_sh,
+                             const int32_t* n_idx, int max_n_idx,
+                             int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                             int causal_tail, float* out, float* lse,
+                             int num_splits, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * svlm_verify - acceptance of gamma drafted tokens.
  * SVLM_VERIFY_GREEDY [StD-dec]: a_i = argmax target[b,i,:] (lowest index on
  *   ties); n = length of the longest prefix with draft_tok[b,j] == a_j;

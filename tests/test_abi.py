@@ -69,6 +69,29 @@ def test_decode_attn_rejects_bad_arguments(lib):
     assert b"16-byte" in lib.svlm_last_error()
 
 
+def _attn_idx(lib, **kw):
+    args = dict(q=NULL, q_sb=0, k=NULL, v=NULL, kv_sb=0, kv_sh=0, kv_sn=128, kv_rows=100, kv_idx=NULL, idx_sb=0,
+                idx_sh=0, n_idx=NULL, max_n_idx=10, dtype=L.SVLM_BF16, batch=1, nq=1, Hq=8, Hkv=2, D=128,
+                scale=0.1, causal=0, out=NULL, lse=NULL, num_splits=0, ws=NULL, ws_bytes=0, stream=NULL)
+    args.update(kw)
+    return lib.svlm_decode_attn_indexed(*args.values())
+
+
+def test_decode_attn_indexed_rejects_bad_arguments(lib):
+    fake = C.c_void_p(4096)   # never dereferenced: validation fails first
+    ok = dict(q=fake, k=fake, v=fake, kv_idx=fake, n_idx=fake, out=fake)
+    assert _attn_idx(lib, **dict(ok, kv_idx=NULL)) == L.SVLM_E_INVALID
+    assert b"index" in lib.svlm_last_error()
+    assert _attn_idx(lib, kv_rows=0, **ok) == L.SVLM_E_INVALID
+    assert _attn_idx(lib, kv_rows=1 << 24, **ok) == L.SVLM_E_INVALID   # 2^24 rows x 256 B > 2^31
+    assert _attn_idx(lib, idx_sh=-1, **ok) == L.SVLM_E_INVALID
+    assert _attn_idx(lib, D=96, **ok) == L.SVLM_E_UNSUPPORTED
+    # a long list needs more splits than asked for: the split length is capped
+    # (the split's list is staged on chip), so the workspace is never zero
+    assert lib.svlm_decode_attn_indexed_workspace(1, 1, 8, 2, 128, 10000, 1) > 0
+    assert lib.svlm_decode_attn_workspace(1, 1, 8, 2, 128, 10000, 1) == 0
+
+
 def test_verify_select_gather_score_reject_bad_arguments(lib):
     fake = C.c_void_p(4096)
     assert lib.svlm_verify(7, 1, 1, 10, fake, fake, fake, fake, fake, fake, fake, 1 << 20, NULL) == L.SVLM_E_INVALID

@@ -52,7 +52,16 @@ struct AttnArgs {
   float* lse;
   float* ws_o;   // [B*Hkv*rows][splits][D]
   float* ws_ml;  // [B*Hkv*rows][splits][2]
+  // indexed variant: key position p of (b, h) is cache row kv_idx[b * idx_sb + h * idx_sh + p]
+  // of the kv_rows rows at k + b * kv_sb + h * kv_sh (and likewise for v)
+  const int32_t* kv_idx;
+  int64_t idx_sb, idx_sh;
+  int kv_rows;
 };
+
+// keys per split when the keys are addressed through an index list (the
+// split's indices are staged in LDS)
+constexpr int kMaxIdxSplit = 2048;
 
 constexpr int kWaves = 4;                  // waves per workgroup
 constexpr int kBlock = 16;                 // keys per wave per step (one MFMA block)
@@ -84,7 +93,10 @@ constexpr int ring_depth() {
 // every query row of the chunk (RB blocks of 16 rows), staging its own blocks
 // through a private ring of NS slots in LDS.  The waves' partial states are
 // merged through LDS in wave order at the end.
-template <int D, int RB, int NS>
+// IDX: the keys are the rows named by an index list (a draft that reads the
+// selected rows of the full cache in place, no compact copy); the row
+// positions p below are then positions in the list.
+template <int D, int RB, int NS, bool IDX>
 __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   constexpr int KK = D / 32;             // 32-wide d chunks of the QK product
   constexpr int DV = D / 16;             // d values per lane in the PV product
@@ -133,20 +145,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
 
   // Range-checked buffer descriptors over exactly this split's keys: transfers
   // past k_end deliver zeros without touching memory, so every transfer is
-  // issued unconditionally and the wait counts are static.
+  // issued unconditionally and the wait counts are static.  Indexed keys: the
+  // descriptors cover the whole cache of (b, h) and a position past the list
+  // (or an index outside the cache) gets an offset past the end, which reads
+  // zeros the same way.
   const int64_t row_bytes = a.kv_sn * 2;
   const int n_rows = max(k_end - k_begin, 0);
-  const int64_t off0 = (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh + (int64_t)k_begin * a.kv_sn;
+  const int64_t off0 = (int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh + (IDX ? 0 : (int64_t)k_begin * a.kv_sn);
+  const int range = IDX ? (int)(a.kv_rows * row_bytes) : (int)(n_rows * row_bytes);
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + off0), (short)0, range, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + off0), (short)0, (int)(n_rows * row_bytes), kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + off0), (short)0, range, kBufferFlags);
+  __shared__ int sm_idx[IDX ? kMaxIdxSplit : 1];
+  if constexpr (IDX) {
+    const int32_t* idx = a.kv_idx + (int64_t)b * a.idx_sb + (int64_t)h * a.idx_sh;
+    for (int p = threadIdx.x; p < a.keys_per_split; p += 64 * kWaves) {
+      int r = -1;
+      if (k_begin + p < k_end) {
+        r = idx[k_begin + p];
+        if (r < 0 || r >= a.kv_rows) r = -1;
+      }
+      sm_idx[p] = r;
+    }
+    __syncthreads();
+  }
 
   // Stage block j of this wave (16 K rows, then the same 16 V rows) into ring
   // slot `slot`: transfer i moves 1 KB = 1024 / ROWB rows, 16-byte chunks
   // XOR-swizzled by row (chunk p of row r holds source chunk p ^ (r % CH));
   // lane l lands at slot + 1 KB * i + 16 l.  The per-lane part of each source
-  // offset is fixed; the block's first row enters as the scalar offset.
+  // offset is fixed; the block's first row enters as the scalar offset (or,
+  // indexed, each lane's row comes from the staged list).
   // Nontemporal: each byte is read once.
   static_assert(NQ <= 4, "transfers per block");
   int src_lane[4] = {0, 0, 0, 0};
@@ -154,18 +184,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   for (int i = 0; i < NQ; ++i) {
     const int r = i * (1024 / ROWB) + lane / CH;
     const int p = lane % CH;
-    src_lane[i] = r * (int)row_bytes + ((p ^ (r % CH)) * 16);
+    src_lane[i] = (IDX ? 0 : r * (int)row_bytes) + ((p ^ (r % CH)) * 16);
   }
   auto stage = [&](int slot, int j) {
     unsigned char* base = my_ring + slot * SLOT;
-    const int soff = (j * kStep + kBlock * wave) * (int)row_bytes;  // first row of the block, in bytes
+    int soff = (j * kStep + kBlock * wave) * (int)row_bytes;  // first row of the block, in bytes
+    int voff[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) voff[i] = src_lane[i];
+    if constexpr (IDX) {
+      soff = 0;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int pos = j * kStep + kBlock * wave + i * (1024 / ROWB) + lane / CH;  // in the split
+        const int r = (pos < a.keys_per_split) ? sm_idx[pos] : -1;
+        voff[i] = (r >= 0) ? r * (int)row_bytes + src_lane[i] : range;
+      }
+    }
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
       for (int i = 0; i < NQ; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kv ? vrs : krs,
                                                  (__attribute__((address_space(3))) void*)(base + kv * QB + i * 1024),
-                                                 16, src_lane[i], soff, 0, kNT);
+                                                 16, voff[i], soff, 0, kNT);
   };
 
   // ---- query rows in registers (B operand of S^T = K Q^T): lane (c, g4) holds
@@ -532,7 +574,8 @@ void launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
 template <int D, int RB>
 void launch_rb(const AttnArgs& a, int batch, int row_chunks, hipStream_t st) {
   dim3 grid((unsigned)(batch * a.Hkv * a.splits), (unsigned)row_chunks);
-  attn_splitk<D, RB, ring_depth<D>()><<<grid, 64 * kWaves, 0, st>>>(a);
+  if (a.kv_idx) attn_splitk<D, RB, ring_depth<D>(), true><<<grid, 64 * kWaves, 0, st>>>(a);
+  else attn_splitk<D, RB, ring_depth<D>(), false><<<grid, 64 * kWaves, 0, st>>>(a);
 }
 
 template <int D>
@@ -556,7 +599,10 @@ struct Plan {
 
 constexpr int kMinStepsPerSplit = 2;  // shorter splits cost more in fixed latency than they add in parallelism
 
-Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
+// max_steps_per_split > 0 caps the split length (indexed keys: the split's
+// list is staged in LDS)
+Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int num_splits,
+               int max_steps_per_split = 0) {
   Plan p;
   const int rows = (Hq / Hkv) * nq;
   const int max_rb = (D == 128) ? kMaxRB128 : kMaxRB64;
@@ -576,6 +622,7 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
     splits = std::min(splits, std::max(1, steps / kMinStepsPerSplit));
   }
   splits = std::max(1, std::min(splits, steps));
+  if (max_steps_per_split > 0) splits = std::max(splits, (steps + max_steps_per_split - 1) / max_steps_per_split);
   const int steps_per_split = (steps + splits - 1) / splits;
   p.keys_per_split = steps_per_split * kStep;
   p.splits = (max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
@@ -601,38 +648,41 @@ WsLayout ws_layout(const Plan& p, int batch, int Hq, int nq, int D) {
 
 using namespace svlm;
 
-extern "C" size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len,
-                                             int num_splits) {
-  if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_kv_len < 1) return 0;
-  const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
-  return ws_layout(p, batch, Hq, nq, D).total;
-}
+namespace {
+constexpr int kIdxMaxSteps = kMaxIdxSplit / kStep;
 
-extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
-                                int64_t kv_sh, int64_t kv_sn, const int32_t* kv_len, int max_kv_len, int dtype,
-                                int batch, int nq, int Hq, int Hkv, int D, float scale, int causal_tail,
-                                float* out, float* lse, int num_splits, void* ws, size_t ws_bytes,
-                                void* stream) {
-  if (dtype != SVLM_BF16) return fail(SVLM_E_UNSUPPORTED, "svlm_decode_attn: only SVLM_BF16 operands are supported");
-  if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "svlm_decode_attn: D must be 64 or 128 (got %d)", D);
-  if (!q || !k || !v || !kv_len || !out) return fail(SVLM_E_INVALID, "svlm_decode_attn: null pointer");
+// shared by the contiguous and the indexed entry points; kv_idx == nullptr
+// means keys are rows 0 .. kv_len - 1 of the cache
+int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
+                     int64_t kv_sh, int64_t kv_sn, const int32_t* kv_idx, int64_t idx_sb, int64_t idx_sh,
+                     int kv_rows, const int32_t* kv_len, int max_kv_len, int dtype, int batch, int nq, int Hq,
+                     int Hkv, int D, float scale, int causal_tail, float* out, float* lse, int num_splits, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (dtype != SVLM_BF16) return fail(SVLM_E_UNSUPPORTED, "%s: only SVLM_BF16 operands are supported", name);
+  if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", name, D);
+  if (!q || !k || !v || !kv_len || !out) return fail(SVLM_E_INVALID, "%s: null pointer", name);
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || max_kv_len < 1)
-    return fail(SVLM_E_INVALID, "svlm_decode_attn: batch, nq, Hq, Hkv, max_kv_len must be >= 1");
-  if (Hq % Hkv) return fail(SVLM_E_INVALID, "svlm_decode_attn: Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (causal_tail != 0 && causal_tail != 1) return fail(SVLM_E_INVALID, "svlm_decode_attn: causal_tail must be 0 or 1");
-  if (!std::isfinite(scale)) return fail(SVLM_E_INVALID, "svlm_decode_attn: scale must be finite");
+    return fail(SVLM_E_INVALID, "%s: batch, nq, Hq, Hkv and the key count bound must be >= 1", name);
+  if (Hq % Hkv) return fail(SVLM_E_INVALID, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
+  if (causal_tail != 0 && causal_tail != 1) return fail(SVLM_E_INVALID, "%s: causal_tail must be 0 or 1", name);
+  if (!std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(SVLM_E_INVALID, "svlm_decode_attn: q, k, v, out must be 16-byte aligned");
+    return fail(SVLM_E_INVALID, "%s: q, k, v, out must be 16-byte aligned", name);
   if (kv_sn < D || kv_sn % 8 || kv_sh % 8 || kv_sb % 8 || kv_sh < 0 || kv_sb < 0)
-    return fail(SVLM_E_INVALID, "svlm_decode_attn: KV strides must be multiples of 8 elements with kv_sn >= D");
+    return fail(SVLM_E_INVALID, "%s: KV strides must be multiples of 8 elements with kv_sn >= D", name);
   if (q_sb % 8 || (batch > 1 && q_sb < (int64_t)nq * Hq * D))
-    return fail(SVLM_E_INVALID, "svlm_decode_attn: q batch stride must be a multiple of 8 and >= nq*Hq*D");
-  if (num_splits < 0) return fail(SVLM_E_INVALID, "svlm_decode_attn: num_splits must be >= 0");
-  const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
-  const size_t need = svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
+    return fail(SVLM_E_INVALID, "%s: q batch stride must be a multiple of 8 and >= nq*Hq*D", name);
+  if (num_splits < 0) return fail(SVLM_E_INVALID, "%s: num_splits must be >= 0", name);
+  if (kv_idx) {
+    if (kv_rows < 1 || (int64_t)kv_rows * kv_sn * 2 > INT32_MAX)
+      return fail(SVLM_E_INVALID, "%s: kv_rows must be >= 1 with kv_rows * kv_sn * 2 < 2^31", name);
+    if (idx_sb < 0 || idx_sh < 0) return fail(SVLM_E_INVALID, "%s: index strides must be >= 0", name);
+  }
+  const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits, kv_idx ? kIdxMaxSteps : 0);
+  const size_t need = ws_layout(p, batch, Hq, nq, D).total;
   if (need > 0 && (!ws || ws_bytes < need))
-    return fail(SVLM_E_WORKSPACE, "svlm_decode_attn: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (need > 0 && !aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_decode_attn: workspace must be 16-byte aligned");
+    return fail(SVLM_E_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", name, need, ws_bytes);
+  if (need > 0 && !aligned16(ws)) return fail(SVLM_E_INVALID, "%s: workspace must be 16-byte aligned", name);
 
   AttnArgs a;
   a.q = (const uint16_t*)q;
@@ -656,6 +706,10 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
   a.keys_per_split = p.keys_per_split;
   a.out = out;
   a.lse = lse;
+  a.kv_idx = kv_idx;
+  a.idx_sb = idx_sb;
+  a.idx_sh = idx_sh;
+  a.kv_rows = kv_rows;
   const WsLayout wl = ws_layout(p, batch, Hq, nq, D);
   a.ws_o = ws ? (float*)((char*)ws + wl.o_off) : nullptr;
   a.ws_ml = ws ? (float*)((char*)ws + wl.ml_off) : nullptr;
@@ -666,5 +720,42 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
     if (D == 128) launch_combine<128>(a, batch, st);
     else launch_combine<64>(a, batch, st);
   }
-  return check_launch("svlm_decode_attn");
+  return check_launch(name);
+}
+}  // namespace
+
+extern "C" size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len,
+                                             int num_splits) {
+  if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_kv_len < 1) return 0;
+  const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
+  return ws_layout(p, batch, Hq, nq, D).total;
+}
+
+extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
+                                int64_t kv_sh, int64_t kv_sn, const int32_t* kv_len, int max_kv_len, int dtype,
+                                int batch, int nq, int Hq, int Hkv, int D, float scale, int causal_tail,
+                                float* out, float* lse, int num_splits, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return decode_attn_impl("svlm_decode_attn", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, nullptr, 0, 0, 0, kv_len,
+                          max_kv_len, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse, num_splits, ws,
+                          ws_bytes, stream);
+}
+
+extern "C" size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_n_idx,
+                                                     int num_splits) {
+  if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_n_idx < 1) return 0;
+  const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_n_idx, num_splits, kIdxMaxSteps);
+  return ws_layout(p, batch, Hq, nq, D).total;
+}
+
+extern "C" int svlm_decode_attn_indexed(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
+                                        int64_t kv_sh, int64_t kv_sn, int kv_rows, const int32_t* kv_idx,
+                                        int64_t idx_sb, int64_t idx_sh, const int32_t* n_idx, int max_n_idx,
+                                        int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                                        int causal_tail, float* out, float* lse, int num_splits, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (!kv_idx) return fail(SVLM_E_INVALID, "svlm_decode_attn_indexed: null index list");
+  return decode_attn_impl("svlm_decode_attn_indexed", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, kv_idx, idx_sb, idx_sh,
+                          kv_rows, n_idx, max_n_idx, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse,
+                          num_splits, ws, ws_bytes, stream);
 }

@@ -158,6 +158,67 @@ def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch
     return out, lse
 
 
+def decode_attn_indexed_workspace_bytes(batch, nq, Hq, Hkv, D, max_n_idx, num_splits=0) -> int:
+    return int(L.load().svlm_decode_attn_indexed_workspace(batch, nq, Hq, Hkv, D, max_n_idx, num_splits))
+
+
+def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
+                        n_idx: torch.Tensor, causal_tail: bool, scale: float | None = None, num_splits: int = 0,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None, want_lse: bool = True):
+    """Decode attention over cache rows named by kv_idx, read in place.
+
+    q [B][nq][Hq][D]; k, v [B][Hkv][rows][D] or [Hkv][rows][D]; kv_idx int32
+    [n] (one list), [Hkv][n] (per head) or [B][Hkv][n]; n_idx int32 [B] (list
+    lengths) -> (out fp32, lse fp32)."""
+    _dev(q, k, v, kv_idx, n_idx, out, lse, ws)
+    _bf16(q, k, v)
+    B, nq, Hq, D = q.shape
+    if q[0].stride() != (Hq * D, D, 1):
+        raise ValueError("q must be contiguous inside each batch entry")
+    if k.dim() == 3:
+        if B != 1:
+            raise ValueError("3-D KV means batch 1")
+        kv_sb = 0
+        Hkv, rows, _ = k.shape
+        kv_sh, kv_sn = k.stride(0), k.stride(1)
+    else:
+        Hkv, rows = k.shape[1], k.shape[2]
+        kv_sb, kv_sh, kv_sn = k.stride(0) if B > 1 else 0, k.stride(1), k.stride(2)
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must have identical shapes and strides")
+    if kv_idx.dtype != torch.int32 or kv_idx.stride(-1) != 1:
+        raise ValueError("kv_idx must be int32 with a contiguous last axis")
+    if kv_idx.dim() == 1:
+        idx_sb, idx_sh = 0, 0
+    elif kv_idx.dim() == 2:
+        if kv_idx.shape[0] != Hkv:
+            raise ValueError("2-D kv_idx must be [Hkv][n]")
+        idx_sb, idx_sh = 0, kv_idx.stride(0)
+    else:
+        if tuple(kv_idx.shape[:2]) != (B, Hkv):
+            raise ValueError("3-D kv_idx must be [B][Hkv][n]")
+        idx_sb, idx_sh = kv_idx.stride(0), kv_idx.stride(1)
+    max_n = kv_idx.shape[-1]
+    if n_idx.dtype != torch.int32 or n_idx.numel() != B:
+        raise ValueError("n_idx must be int32 [B]")
+    q_sb = q.stride(0) if B > 1 else nq * Hq * D
+    if out is None:
+        out = torch.empty(B, nq, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
+    need = decode_attn_indexed_workspace_bytes(B, nq, Hq, Hkv, D, max_n, num_splits)
+    if ws is None and need > 0:
+        ws = _ws(need, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L.call("svlm_decode_attn_indexed", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn, rows,
+           kv_idx.data_ptr(), idx_sb, idx_sh, n_idx.data_ptr(), max_n, L.SVLM_BF16, B, nq, Hq, Hkv, D,
+           float(scale), 1 if causal_tail else 0, out.data_ptr(), lse.data_ptr() if lse is not None else None,
+           num_splits, ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream())
+    return out, lse
+
+
 # ---------------------------------------------------------------------------
 def verify_workspace_bytes(batch, gamma, V) -> int:
     return int(L.load().svlm_verify_workspace(batch, gamma, V))

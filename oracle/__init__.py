@@ -25,7 +25,9 @@ Sources, cited by page title and section:
   * ParallelVLM notes (CVPR 2026), background and "parallel decoding":
     drafted tokens are accepted by rejection sampling, so the output
     distribution is the target's; a rejected token is resampled from the
-    target.
+    target.  Method section 1, "UV-Prune": video tokens scored by the change,
+    across early target layers, of their cosine similarity to the text
+    tokens, summed over the text; top-K by the pruning ratio.
 
 Parity status: every function here is pinned by tests that do not reuse its
 code (brute force, closed forms, invariants, library routines); see
@@ -36,10 +38,12 @@ from .select import select_row, select_rows, FIXED_POINT_SHIFT
 from .gather import gather_kv
 from .attention import decode_attn
 from .verify import verify_greedy, verify_reject, sample_fixed_point
+from .uvprune import cosine_matrix, uvprune_scores, uvprune_keep
 
 __all__ = [
     "attention_probs", "score_layer", "aggregate_heads", "score_rows_for_config",
     "select_row", "select_rows", "FIXED_POINT_SHIFT",
     "gather_kv", "decode_attn",
     "verify_greedy", "verify_reject", "sample_fixed_point",
+    "cosine_matrix", "uvprune_scores", "uvprune_keep",
 ]

@@ -128,6 +128,12 @@ def main():
     ws_d = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)), dtype=torch.uint8, device=dev)
     ws_di = torch.empty(max(256, ops.decode_attn_indexed_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)),
                         dtype=torch.uint8, device=dev)
+    # UV-Prune alternative to the attention score: hidden states of layers 0 and L at hidden size 8192
+    d_model = W.HIDDEN[cfg.name]
+    hv = torch.randn(2, NV, d_model, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    hx = torch.randn(2, T, d_model, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    uv_out = torch.empty(NV, dtype=torch.float32, device=dev)
+    ws_uv = torch.empty(max(256, ops.uvprune_workspace_bytes(T, d_model)), dtype=torch.uint8, device=dev)
     # the draft's key list for the in-place variant: kept visual rows, then the text and newest rows
     draft_idx = torch.empty(N_draft, dtype=torch.int32, device=dev)
     draft_idx[B_keep:] = torch.arange(NV, NV + T + 1, dtype=torch.int32, device=dev)
@@ -162,6 +168,9 @@ def main():
     def k_draft_idx(l):
         ops.decode_attn_indexed(qd[l], K[l], Vv[l], draft_idx, kv_len_d, False, out=o_d, lse=l_d, ws=ws_di)
 
+    def k_uvprune():
+        ops.uvprune_score(hv[0], hv[1], hx[0], hx[1], 1.0 / (4 * T), 0.5, out=uv_out, ws=ws_uv)
+
     def k_verify_attn(l):
         ops.decode_attn(qv[l], K[l], Vv[l], kv_len_v, True, out=o_v, lse=l_v, ws=ws_v)
 
@@ -174,11 +183,12 @@ def main():
         "gather": lambda: [k_gather(l) for l in range(L)],
         "draft_attn": lambda: [k_draft(l) for l in range(L)],
         "draft_attn_indexed": lambda: [k_draft_idx(l) for l in range(L)],
+        "uvprune_score": k_uvprune,
         "verify_attn": lambda: [k_verify_attn(l) for l in range(L)],
         "accept": k_accept,
     }
-    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "draft_attn_indexed": L, "verify_attn": L,
-             "accept": 1}
+    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "draft_attn_indexed": L, "uvprune_score": 1,
+             "verify_attn": L, "accept": 1}
 
     # warm up eagerly (also fills the library's device-property cache), then capture
     # each kernel sequence as a HIP graph so host launch overhead is out of the timings
@@ -194,9 +204,10 @@ def main():
         graphs[kind] = gr
     torch.cuda.synchronize()
 
-    # one step of the path: every kind but the in-place draft, which is the
-    # alternative to gather + compact draft and is timed on its own below
-    step_kinds = [k for k in seqs if k != "draft_attn_indexed"]
+    # one step of the path: every kind but the alternatives, timed on their own
+    # below (the in-place draft instead of gather + compact draft; the UV-Prune
+    # score instead of the attention score)
+    step_kinds = [k for k in seqs if k not in ("draft_attn_indexed", "uvprune_score")]
 
     def step():
         for kind in step_kinds:
@@ -262,6 +273,10 @@ def main():
     kernels["draft_attn_indexed"].update(
         bytes=draft_bytes, gbs=round(draft_bytes / (per_us["draft_attn_indexed"] * 1e-6) / 1e9, 1),
         what="the same draft read in place from the full cache through the key list (no gather)")
+    uv_bytes = 2 * (NV + T) * d_model * 2
+    kernels["uvprune_score"].update(
+        bytes=uv_bytes, gbs=round(uv_bytes / (per_us["uvprune_score"] * 1e-6) / 1e9, 1),
+        what="UV-Prune score from layer-0 and layer-L hidden states (hidden 8192), once per prefill")
     kernels["score"].update(flop=score_flop, tflops=round(score_flop / (us_score * 1e-6) / 1e12, 1))
     kernels["gather"].update(bytes=2 * 2 * (B_keep + T) * Hkv * D * 2,
                              gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (per_us["gather"] * 1e-6) / 1e9, 1))

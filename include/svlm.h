@@ -22,6 +22,9 @@
  *                decoding": candidates accepted by rejection sampling, which
  *                keeps the target's output distribution; a rejected token is
  *                resampled from the target.
+ *   [PVLM-UV]    Same page, method section 1 "UV-Prune": video tokens scored
+ *                by the change across early target layers of their cosine
+ *                similarity to the text tokens, summed over the text; top-K.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless a parameter says otherwise.  Sizes
@@ -220,6 +223,30 @@ int svlm_decode_attn_indexed(const void* q, int64_t q_sb,
                              int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
                              int causal_tail, float* out, float* lse,
                              int num_splits, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_uvprune_score - UV-Prune score of every video token (an alternative
+ * to svlm_score's attention signal that needs no attention matrix).
+ * [PVLM-UV] ParallelVLM notes, method section 1 ("UV-Prune").
+ *
+ * With S^l_ij the cosine similarity of video token i and text token j at
+ * target layer l (a zero vector's similarities are 0):
+ *   dS_i = sum_j sum_{l=1..L} (S^l_ij - S^(l-1)_ij) = sum_j (S^L_ij - S^0_ij)
+ *   out[i] = out_scale * dS_i + out_offset
+ * so only the hidden states of layers 0 and L are read.  dS lies in
+ * [-2 n_text, 2 n_text]; out_scale = 1/(4 n_text), out_offset = 1/2 maps it
+ * monotonically into [0, 1] for svlm_select with top_p >= 1 (top-K).
+ * v0, vL: [n_vis][d] bf16 video hidden states of layers 0 and L, row stride
+ *         v_sn; x0, xL: [n_text][d] bf16 text hidden states, row stride x_sn.
+ * out: [n_vis] fp32.  ws: svlm_uvprune_workspace(n_text, d) bytes.
+ * Requires d % 8 == 0, d <= 16384, strides multiples of 8 and >= d,
+ * 16-byte aligned pointers.  fp32 accumulation; deterministic.
+ * ------------------------------------------------------------------------ */
+size_t svlm_uvprune_workspace(int n_text, int d);
+int svlm_uvprune_score(const void* v0, const void* vL, int64_t v_sn, int n_vis,
+                       const void* x0, const void* xL, int64_t x_sn, int n_text, int d,
+                       int dtype, float out_scale, float out_offset, float* out,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * svlm_verify - acceptance of gamma drafted tokens.

@@ -92,6 +92,24 @@ def test_decode_attn_indexed_rejects_bad_arguments(lib):
     assert lib.svlm_decode_attn_workspace(1, 1, 8, 2, 128, 10000, 1) == 0
 
 
+def test_uvprune_rejects_bad_arguments(lib):
+    fake = C.c_void_p(4096)
+    f = lib.svlm_uvprune_score
+    assert f(fake, fake, 256, 10, fake, fake, 256, 4, 256, L.SVLM_F32, 1.0, 0.0, fake, fake, 1 << 20, NULL) \
+        == L.SVLM_E_UNSUPPORTED
+    assert f(fake, fake, 256, 10, fake, fake, 256, 4, 250, L.SVLM_BF16, 1.0, 0.0, fake, fake, 1 << 20, NULL) \
+        == L.SVLM_E_UNSUPPORTED                                       # d % 8
+    assert f(fake, fake, 256, 10, fake, fake, 256, 4, 32768, L.SVLM_BF16, 1.0, 0.0, fake, fake, 1 << 20, NULL) \
+        == L.SVLM_E_UNSUPPORTED                                       # d too large
+    assert f(fake, fake, 128, 10, fake, fake, 256, 4, 256, L.SVLM_BF16, 1.0, 0.0, fake, fake, 1 << 20, NULL) \
+        == L.SVLM_E_INVALID                                           # stride < d
+    assert f(fake, fake, 256, 10, fake, fake, 256, 4, 256, L.SVLM_BF16, float("nan"), 0.0, fake, fake, 1 << 20,
+             NULL) == L.SVLM_E_INVALID
+    assert f(fake, fake, 256, 10, fake, fake, 256, 4, 256, L.SVLM_BF16, 1.0, 0.0, fake, fake, 16, NULL) \
+        == L.SVLM_E_WORKSPACE
+    assert lib.svlm_uvprune_workspace(128, 8192) >= 2 * 8192 * 4
+
+
 def test_verify_select_gather_score_reject_bad_arguments(lib):
     fake = C.c_void_p(4096)
     assert lib.svlm_verify(7, 1, 1, 10, fake, fake, fake, fake, fake, fake, fake, 1 << 20, NULL) == L.SVLM_E_INVALID

@@ -35,6 +35,8 @@ SIGNATURES = {
     "svlm_decode_attn_indexed_workspace": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "svlm_decode_attn_indexed": (i32, [vp, i64, vp, vp, i64, i64, i64, i32, vp, i64, i64, vp, i32, i32, i32, i32,
                                        i32, i32, i32, f32, i32, vp, vp, i32, vp, sz, vp]),
+    "svlm_uvprune_workspace": (sz, [i32, i32]),
+    "svlm_uvprune_score": (i32, [vp, vp, i64, i32, vp, vp, i64, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
     "svlm_verify_workspace": (sz, [i32, i32, i32]),
     "svlm_verify": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
 }

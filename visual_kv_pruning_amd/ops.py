@@ -220,6 +220,35 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
 
 
 # ---------------------------------------------------------------------------
+def uvprune_workspace_bytes(n_text: int, d: int) -> int:
+    return int(L.load().svlm_uvprune_workspace(n_text, d))
+
+
+def uvprune_score(v0: torch.Tensor, vL: torch.Tensor, x0: torch.Tensor, xL: torch.Tensor,
+                  out_scale: float = 1.0, out_offset: float = 0.0, out: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None) -> torch.Tensor:
+    """UV-Prune score.  v0, vL [n_vis][d], x0, xL [n_text][d] bf16 hidden states of
+    layers 0 and L -> out [n_vis] fp32 = out_scale * dS + out_offset."""
+    _dev(v0, vL, x0, xL, out, ws)
+    _bf16(v0, vL, x0, xL)
+    if v0.shape != vL.shape or x0.shape != xL.shape or v0.shape[1] != x0.shape[1]:
+        raise ValueError("v0/vL and x0/xL must have matching shapes and the same hidden size")
+    if v0.stride() != vL.stride() or x0.stride() != xL.stride() or v0.stride(1) != 1 or x0.stride(1) != 1:
+        raise ValueError("rows must be contiguous, with the same strides for both layers")
+    n_vis, d = v0.shape
+    n_text = x0.shape[0]
+    if out is None:
+        out = torch.empty(n_vis, dtype=torch.float32, device=v0.device)
+    need = uvprune_workspace_bytes(n_text, d)
+    if ws is None:
+        ws = _ws(need, v0.device)
+    L.call("svlm_uvprune_score", v0.data_ptr(), vL.data_ptr(), v0.stride(0), n_vis, x0.data_ptr(), xL.data_ptr(),
+           x0.stride(0), n_text, d, L.SVLM_BF16, float(out_scale), float(out_offset), out.data_ptr(),
+           ws.data_ptr(), ws.numel(), _stream())
+    return out
+
+
+# ---------------------------------------------------------------------------
 def verify_workspace_bytes(batch, gamma, V) -> int:
     return int(L.load().svlm_verify_workspace(batch, gamma, V))
 

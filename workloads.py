@@ -98,7 +98,7 @@ CONFIGS = {c.index: c for c in (C1, C2, C3, C4, C5)}
 # tensor ids for the seed spawn keys
 _IDS = {name: i for i, name in enumerate(
     ("q_text", "k", "v", "salient", "q_dec", "k_new", "v_new", "logits", "draft_noise",
-     "draft_tok", "uniform", "scores", "misc", "span_starts"))}
+     "draft_tok", "uniform", "scores", "misc", "span_starts", "hidden_v", "hidden_x"))}
 
 
 def rng_for(cfg_index: int, name: str, layer: int = 0, extra: int = 0) -> np.random.Generator:
@@ -296,3 +296,36 @@ def score_rows(kind: str, rows: int, n: int, seed: int = 0) -> np.ndarray:
     if np.any(over):
         x[over] = (x[over].astype(np.float64) * (1.0 - 1e-6)).astype(np.float32)
     return x
+
+
+# ---------------------------------------------------------------------------
+# hidden states for the UV-Prune score (layers 0 .. n_layers)
+# ---------------------------------------------------------------------------
+
+# hidden size of the model family each config is shaped like
+HIDDEN = {"tiny_ref": 256, "qwen2vl7b_8k": 3584, "llavaov72b_25k": 8192, "qwen25vl32b_20k": 5120,
+          "hour_std_141k": 3584}
+
+
+def uv_hidden(cfg: Config, n_layers: int = 2, d_model: int | None = None, extra: int = 0):
+    """Video [n_layers+1][n_vis][d] and text [n_layers+1][n_text][d] hidden states (bf16 values).
+
+    Every vector is N(0,1) noise plus, for the text, a shared direction u; the
+    salient video tokens (the same positions as the attention value model)
+    drift towards u with depth (weight 3 l / n_layers at layer l), so they
+    gain alignment with the text across the layers."""
+    d = d_model or HIDDEN[cfg.name]
+    rng_v = rng_for(cfg.index, "hidden_v", 0, extra)
+    rng_x = rng_for(cfg.index, "hidden_x", 0, extra)
+    u = _normal(rng_x, (d,))
+    u = u / np.float32(np.sqrt(float((u.astype(np.float64) ** 2).sum()) / d))   # unit RMS direction
+    sal = salient_positions(cfg)
+    vs, xs = [], []
+    for l in range(n_layers + 1):
+        v = _normal(rng_v, (cfg.n_vis, d))
+        v[sal] += np.float32(3.0 * l / n_layers) * u
+        x = _normal(rng_x, (cfg.n_text, d)) + np.float32(2.0) * u
+        vs.append(bf16_round(v))
+        xs.append(bf16_round(x))
+    return vs, xs
+

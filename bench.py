@@ -341,6 +341,10 @@ def main():
         "kernels": kernels,
         "parallel_decoding": {
             "us_per_step": round(pd_us, 2),
+            # ParallelVLM "parallel decoding": window gamma = c* = T_p / T_q(alpha), here with the
+            # attention times alone (dense verify call over one draft call, per layer)
+            "speed_ratio_attn": round(us_verify / us_draft, 2),
+            "window_gamma_attn": max(1, round(us_verify / us_draft)),
             "gbs": round(L * (verify_bytes + draft_bytes) / (pd_us * 1e-6) / 1e9, 1),
             "what": "80 dense-verify and 80 draft launches overlapped on two streams (one graph, two branches); "
                     "decode_attn_us_per_step runs them one after the other"},

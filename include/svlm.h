@@ -102,7 +102,9 @@ const char* svlm_last_error(void);
  * ws:     svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis) bytes (per-split row
  *         statistics and per-head score rows).
  * Requires 1 <= T <= 128, scale > 0, q_pos0 + T <= n_ctx, 0 <= vis_start, vis_start + n_vis
- * <= q_pos0 + 1 (every visual key visible to every text query).
+ * <= q_pos0 + 1 (every visual key visible to every text query), n_vis <= 2^18,
+ * and ((T-1)*q_st + D)*2 and (n_ctx + 1024)*k_sn*2 below 2^31 (32-bit buffer
+ * ranges; SVLM_E_UNSUPPORTED otherwise).
  * Computes QK^T on bf16 matrix cores with fp32 accumulation, in two passes
  * (row log-sum-exp, then normalised column sums); the score matrix is never
  * stored.
@@ -165,8 +167,9 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
 /* ------------------------------------------------------------------------
  * svlm_decode_attn - split-K grouped-query decode attention, draft or verify.
  * [StD-dec] (sparse draft over the kept KV, one query; dense verify of the
- * gamma+1 newest tokens in one pass over the full KV); [SpecVLM-5] / page 1
- * section 4 (decode is bound by loading the KV cache every step).
+ * gamma+1 newest tokens in one pass over the full KV); SpecVLM
+ * technology-transfer listing, section 4 (decode is bound by loading the KV
+ * cache every step).
  *
  * For batch b, query i < nq and q head h (g = h / (Hq/Hkv)), keys
  * n < L(b,i) with L = kv_len[b] - nq + i + 1 if causal_tail else kv_len[b]:
@@ -183,6 +186,9 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
  * ws: svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits)
  *   bytes (0 when one split suffices); no initial contents are needed.  Two
  *   calls that overlap in time must not share a workspace.
+ * Requires scale > 0, nq*Hq*D*2 < 2^31, and one key split's rows times
+ * kv_sn*2 below 2^31 bytes (always true when (max_kv_len + 576)*kv_sn*2 <
+ * 2^31; SVLM_E_UNSUPPORTED otherwise).
  * Works in bf16 matrix-core products with fp32 accumulation; the softmax
  * weights enter the value product as a bf16 hi + lo pair, so the output
  * keeps fp32-level accuracy.

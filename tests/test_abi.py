@@ -63,6 +63,11 @@ def test_decode_attn_rejects_bad_arguments(lib):
     assert _attn(lib, Hq=6, Hkv=4, **ok) == L.SVLM_E_INVALID          # Hq % Hkv
     assert _attn(lib, nq=0, **ok) == L.SVLM_E_INVALID
     assert _attn(lib, scale=float("inf"), **ok) == L.SVLM_E_INVALID
+    assert _attn(lib, scale=0.0, **ok) == L.SVLM_E_INVALID             # the row maxima assume scale > 0
+    assert _attn(lib, scale=-0.1, **ok) == L.SVLM_E_INVALID
+    assert _attn(lib, nq=4096, Hq=4096, Hkv=4096, **ok) == L.SVLM_E_UNSUPPORTED   # queries past a 32-bit range
+    assert _attn(lib, max_kv_len=1 << 23, num_splits=1, **ok) == L.SVLM_E_UNSUPPORTED  # one split past 2^31 bytes
+    assert b"2^31" in lib.svlm_last_error()
     assert _attn(lib, causal=2, **ok) == L.SVLM_E_INVALID
     assert _attn(lib, kv_sn=100, **ok) == L.SVLM_E_INVALID            # row stride not a multiple of 8
     assert _attn(lib, q=C.c_void_p(4098), k=fake, v=fake, kv_len=fake, out=fake) == L.SVLM_E_INVALID  # misaligned
@@ -137,3 +142,6 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     args[15] = 0.1
     args[16] = 9
     assert lib.svlm_score(*args) == L.SVLM_E_INVALID
+    args[16] = 2
+    args[1] = 1 << 27                        # one head's queries past a 32-bit buffer range
+    assert lib.svlm_score(*args) == L.SVLM_E_UNSUPPORTED

@@ -665,7 +665,7 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
     return fail(SVLM_E_INVALID, "%s: batch, nq, Hq, Hkv and the key count bound must be >= 1", name);
   if (Hq % Hkv) return fail(SVLM_E_INVALID, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
   if (causal_tail != 0 && causal_tail != 1) return fail(SVLM_E_INVALID, "%s: causal_tail must be 0 or 1", name);
-  if (!std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite", name);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite and > 0", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(SVLM_E_INVALID, "%s: q, k, v, out must be 16-byte aligned", name);
   if (kv_sn < D || kv_sn % 8 || kv_sh % 8 || kv_sb % 8 || kv_sh < 0 || kv_sb < 0)
@@ -678,7 +678,14 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
       return fail(SVLM_E_INVALID, "%s: kv_rows must be >= 1 with kv_rows * kv_sn * 2 < 2^31", name);
     if (idx_sb < 0 || idx_sh < 0) return fail(SVLM_E_INVALID, "%s: index strides must be >= 0", name);
   }
+  // buffer-descriptor ranges and offsets are 32-bit: one batch entry's
+  // queries, and one split's keys (plus the blocks staged past its end)
+  if ((int64_t)nq * Hq * D * 2 > INT32_MAX)
+    return fail(SVLM_E_UNSUPPORTED, "%s: nq * Hq * D * 2 must be below 2^31", name);
   const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits, kv_idx ? kIdxMaxSteps : 0);
+  if (!kv_idx && ((int64_t)p.keys_per_split + 8 * kStep) * kv_sn * 2 > INT32_MAX)
+    return fail(SVLM_E_UNSUPPORTED, "%s: one key split spans %lld rows of %lld bytes; must stay below 2^31 bytes",
+                name, (long long)p.keys_per_split, (long long)(kv_sn * 2));
   const size_t need = ws_layout(p, batch, Hq, nq, D).total;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SVLM_E_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", name, need, ws_bytes);

@@ -625,6 +625,10 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
   if (!aligned16(q_text) || !aligned16(k)) return fail(SVLM_E_INVALID, "svlm_score: q_text and k must be 16-byte aligned");
   if (q_st % 8 || q_sh % 8 || k_sh % 8 || k_sn % 8 || k_sn < D || q_st < 0 || q_sh < 0 || k_sh < 0)
     return fail(SVLM_E_INVALID, "svlm_score: strides must be non-negative multiples of 8 elements, k_sn >= D");
+  // buffer-descriptor ranges and offsets are 32-bit: one head's text queries,
+  // and one KV head's keys (plus the tiles staged past a split's end)
+  if (((int64_t)(T - 1) * q_st + D) * 2 > INT32_MAX || ((int64_t)n_ctx + 1024) * k_sn * 2 > INT32_MAX)
+    return fail(SVLM_E_UNSUPPORTED, "svlm_score: (T-1) * q_st + D and (n_ctx + 1024) * k_sn must stay below 2^30 elements");
   ScoreArgs a;
   a.q = (const uint16_t*)q_text;
   a.q_st = q_st;

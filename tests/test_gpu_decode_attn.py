@@ -184,3 +184,24 @@ def test_wide_score_range(scale_q):
     v = _rand(63, 2, 3000, 128)
     for splits in (1, 7):
         _check(q, k, v, [3000], True, num_splits=splits, name=f"wide range q x{scale_q:g} splits {splits}")
+
+
+def test_binding_rejects_misshaped_outputs():
+    """The library sees only pointers, so the binding refuses caller-supplied
+    outputs that are not exactly what the kernels write."""
+    from visual_kv_pruning_amd import ops
+    log("decode_attn case binding output checks")
+    qd = dev_bf16(_rand(51, 1, 2, 8, 64))
+    kd = dev_bf16(_rand(52, 2, 100, 64))
+    kl = torch.tensor([100], dtype=torch.int32, device="cuda:0")
+    with pytest.raises(ValueError):
+        ops.decode_attn(qd, kd, kd, kl, True, out=torch.empty(1, 2, 8, 32, device="cuda:0"))
+    with pytest.raises(ValueError):
+        ops.decode_attn(qd, kd, kd, kl, True, lse=torch.empty(1, 2, 4, device="cuda:0"))
+    with pytest.raises(ValueError):
+        ops.gather_kv(kd, kd, torch.arange(10, dtype=torch.int32, device="cuda:0"), 90, 10,
+                      k_dst=torch.empty(2, 19, 64, dtype=torch.bfloat16, device="cuda:0"),
+                      v_dst=torch.empty(2, 19, 64, dtype=torch.bfloat16, device="cuda:0"))
+    with pytest.raises(ValueError):
+        ops.gather_kv(kd, kd, torch.arange(10, dtype=torch.int32, device="cuda:0"),
+                      k_dst=torch.empty(2, 10, 64, dtype=torch.bfloat16, device="cuda:0"))

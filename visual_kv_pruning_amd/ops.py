@@ -38,6 +38,17 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+def _nbytes(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check_out(t: torch.Tensor, shape: tuple, dtype, name: str) -> None:
+    """A caller-supplied output must be exactly what the kernel writes: the
+    library sees only its pointer."""
+    if t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 
 # ---------------------------------------------------------------------------
 def score_workspace_bytes(T: int, Hq: int, Hkv: int, q_pos0: int, n_vis: int) -> int:
@@ -68,7 +79,7 @@ def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_st
         scale = 1.0 / math.sqrt(D)
     L.call("svlm_score", q_text.data_ptr(), q_text.stride(0), q_text.stride(1), k.data_ptr(), k.stride(0),
            k.stride(1), L.SVLM_BF16, T, n_ctx, q_pos0, vis_start, n_vis, Hq, Hkv, D, float(scale), _AGG[agg],
-           float(alpha), float(beta), out.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+           float(alpha), float(beta), out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
     return out
 
 
@@ -103,11 +114,18 @@ def gather_kv(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, tail_start: i
     n_idx = idx.shape[-1]
     idx_sh = 0 if idx.dim() == 1 else idx.stride(0)
     n_out = n_idx + n_tail
+    if (k_dst is None) != (v_dst is None):
+        raise ValueError("give both k_dst and v_dst, or neither")
     if k_dst is None:
         k_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
         v_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
-    if k_dst.stride() != v_dst.stride():
-        raise ValueError("k_dst and v_dst must have the same strides")
+    _bf16(k_dst, v_dst)
+    if k_dst.shape != v_dst.shape or k_dst.stride() != v_dst.stride():
+        raise ValueError("k_dst and v_dst must have the same shape and strides")
+    if k_dst.dim() != 3 or k_dst.shape[0] != Hkv or k_dst.shape[1] < n_out or k_dst.shape[2] != D:
+        raise ValueError(f"k_dst and v_dst must be [Hkv={Hkv}][>= {n_out}][D={D}]")
+    if idx.dim() == 2 and idx.shape[0] != Hkv:
+        raise ValueError("2-D idx must be [Hkv][n_idx]")
     L.call("svlm_gather_kv", k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1), N, idx.data_ptr(), idx_sh,
            n_idx, tail_start, n_tail, k_dst.data_ptr(), v_dst.data_ptr(), k_dst.stride(0), k_dst.stride(1), Hkv, D,
            L.SVLM_BF16, _stream())
@@ -144,8 +162,11 @@ def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch
         raise ValueError("kv_len must be int32 [B]")
     if out is None:
         out = torch.empty(B, nq, Hq, D, dtype=torch.float32, device=q.device)
+    _check_out(out, (B, nq, Hq, D), torch.float32, "out")
     if lse is None and want_lse:
         lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, nq, Hq), torch.float32, "lse")
     need = decode_attn_workspace_bytes(B, nq, Hq, Hkv, D, N, num_splits)
     if ws is None and need > 0:
         ws = _ws(need, q.device)
@@ -154,7 +175,7 @@ def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch
     L.call("svlm_decode_attn", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn,
            kv_len.data_ptr(), N, L.SVLM_BF16, B, nq, Hq, Hkv, D, float(scale), 1 if causal_tail else 0,
            out.data_ptr(), lse.data_ptr() if lse is not None else None, num_splits,
-           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream())
+           ws.data_ptr() if ws is not None else None, _nbytes(ws), _stream())
     return out, lse
 
 
@@ -205,8 +226,11 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
     q_sb = q.stride(0) if B > 1 else nq * Hq * D
     if out is None:
         out = torch.empty(B, nq, Hq, D, dtype=torch.float32, device=q.device)
+    _check_out(out, (B, nq, Hq, D), torch.float32, "out")
     if lse is None and want_lse:
         lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, nq, Hq), torch.float32, "lse")
     need = decode_attn_indexed_workspace_bytes(B, nq, Hq, Hkv, D, max_n, num_splits)
     if ws is None and need > 0:
         ws = _ws(need, q.device)
@@ -215,7 +239,7 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
     L.call("svlm_decode_attn_indexed", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn, rows,
            kv_idx.data_ptr(), idx_sb, idx_sh, n_idx.data_ptr(), max_n, L.SVLM_BF16, B, nq, Hq, Hkv, D,
            float(scale), 1 if causal_tail else 0, out.data_ptr(), lse.data_ptr() if lse is not None else None,
-           num_splits, ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, _stream())
+           num_splits, ws.data_ptr() if ws is not None else None, _nbytes(ws), _stream())
     return out, lse
 
 
@@ -239,12 +263,13 @@ def uvprune_score(v0: torch.Tensor, vL: torch.Tensor, x0: torch.Tensor, xL: torc
     n_text = x0.shape[0]
     if out is None:
         out = torch.empty(n_vis, dtype=torch.float32, device=v0.device)
+    _check_out(out, (n_vis,), torch.float32, "out")
     need = uvprune_workspace_bytes(n_text, d)
     if ws is None:
         ws = _ws(need, v0.device)
     L.call("svlm_uvprune_score", v0.data_ptr(), vL.data_ptr(), v0.stride(0), n_vis, x0.data_ptr(), xL.data_ptr(),
            x0.stride(0), n_text, d, L.SVLM_BF16, float(out_scale), float(out_offset), out.data_ptr(),
-           ws.data_ptr(), ws.numel(), _stream())
+           ws.data_ptr(), _nbytes(ws), _stream())
     return out
 
 
@@ -278,5 +303,5 @@ def verify(mode: str, draft_tok: torch.Tensor, target: torch.Tensor, draft_prob:
         ws = _ws(need, target.device)
     L.call("svlm_verify", m, B, gamma, V, draft_tok.data_ptr(), target.data_ptr(),
            draft_prob.data_ptr() if draft_prob is not None else None, u.data_ptr() if u is not None else None,
-           n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+           n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
     return n_acc, nxt

@@ -60,12 +60,14 @@ def test_tiny_config_verify_and_draft():
     _check(q[:, :1], k[:, rows], v[:, rows], [len(rows)], False, name="tiny draft")
 
 
+# every (G, nq) with every key count that holds the nq new tokens
+_SHAPES = [(G, nq, N) for G, nq in [(1, 1), (2, 5), (5, 10), (7, 1), (8, 6), (8, 1)]
+           for N in [1, 31, 33, 65, 1000, 4099] if N >= nq]
+
+
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G,nq", [(1, 1), (2, 5), (5, 10), (7, 1), (8, 6), (8, 1)])
-@pytest.mark.parametrize("N", [1, 31, 33, 65, 1000, 4099])
+@pytest.mark.parametrize("G,nq,N", _SHAPES)
 def test_shapes_and_ragged_tails(D, G, nq, N):
-    if N < nq:
-        pytest.skip("fewer keys than new queries")
     Hkv = 2
     Hq = G * Hkv
     seed = D * 100000 + G * 1000 + nq * 100 + N

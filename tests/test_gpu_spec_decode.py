@@ -21,15 +21,18 @@ def _video(model, seed, frames=4, gh=7, gw=7, n_text=16):
     return Video(frames, gh, gw, vis.to("cuda:0"), text.to("cuda:0"))
 
 
+@pytest.mark.parametrize("draft_mode", ["compact", "indexed"])
 @pytest.mark.parametrize("seed,gamma", [(1, 4), (2, 9)])
-def test_speculative_equals_dense_greedy(seed, gamma):
+def test_speculative_equals_dense_greedy(seed, gamma, draft_mode):
+    """compact: gather + svlm_decode_attn over the draft cache; indexed:
+    svlm_decode_attn_indexed over the full cache in place."""
     from visual_kv_pruning_amd.spec_decode import TinyDecoder, greedy_dense, speculative
     model = TinyDecoder.random(seed)
     video = _video(model, 100 + seed)
     n_new = 40
-    log(f"spec decode case seed={seed} gamma={gamma}")
+    log(f"spec decode case seed={seed} gamma={gamma} draft={draft_mode}")
     ref = greedy_dense(model, video, n_new)
-    got, acc = speculative(model, video, n_new, gamma=gamma, keep=0.1, top_p=0.5)
+    got, acc = speculative(model, video, n_new, gamma=gamma, keep=0.1, top_p=0.5, draft_mode=draft_mode)
     log(f"  accepted drafts per cycle {acc}")
     assert got == ref
     assert len(acc) >= 1 and all(0 <= a <= gamma for a in acc)

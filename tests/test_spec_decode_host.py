@@ -38,17 +38,24 @@ def _substitutes(monkeypatch):
         v_dst[:] = v[:, rows]
         return k_dst, v_dst
 
+    def decode_attn_indexed(q, k, v, kv_idx, n_idx, causal, want_lse=True, **kw):
+        rows = kv_idx[:int(n_idx[0])].long()
+        o, _ = oracle.decode_attn(q.float().numpy(), k[:, rows].float().numpy()[None],
+                                  v[:, rows].float().numpy()[None], [len(rows)], causal)
+        return torch.from_numpy(o).float(), None
+
     def verify(mode, draft_tok, target, **kw):
         n, tok = oracle.verify_greedy(draft_tok.numpy(), target.numpy())
         return torch.from_numpy(n), torch.from_numpy(tok)
 
-    for name, fn in dict(decode_attn=decode_attn, score=score, select=select, gather_kv=gather_kv,
-                         verify=verify).items():
+    for name, fn in dict(decode_attn=decode_attn, decode_attn_indexed=decode_attn_indexed, score=score,
+                         select=select, gather_kv=gather_kv, verify=verify).items():
         monkeypatch.setattr(ops, name, fn)
 
 
+@pytest.mark.parametrize("draft_mode", ["compact", "indexed"])
 @pytest.mark.parametrize("gamma", [3, 6])
-def test_speculative_loop_equals_greedy_on_host(monkeypatch, gamma):
+def test_speculative_loop_equals_greedy_on_host(monkeypatch, gamma, draft_mode):
     from visual_kv_pruning_amd.spec_decode import TinyDecoder, Video, greedy_dense, speculative
     _substitutes(monkeypatch)
     model = TinyDecoder.random(3, layers=2, d_model=128, hq=4, hkv=2, d=64, vocab=256, device="cpu")
@@ -56,6 +63,6 @@ def test_speculative_loop_equals_greedy_on_host(monkeypatch, gamma):
     video = Video(4, 7, 7, torch.randn(196, model.d_model, generator=g),
                   torch.randint(0, model.vocab, (16,), generator=g))
     ref = greedy_dense(model, video, 24)
-    got, acc = speculative(model, video, 24, gamma=gamma, keep=0.1, top_p=0.5)
+    got, acc = speculative(model, video, 24, gamma=gamma, keep=0.1, top_p=0.5, draft_mode=draft_mode)
     assert got == ref
     assert all(0 <= a <= gamma for a in acc)

@@ -6,7 +6,9 @@ random weights (no RoPE; positions enter only through the causal limit) runs
   prefill (plain torch attention, once)
   -> svlm_score per layer, averaged into one row
   -> svlm_select (Top-P on score mass, then the spatially uniform fill)
-  -> svlm_gather_kv per layer into the draft cache (kept visual rows + text)
+  -> svlm_gather_kv per layer into the draft cache (kept visual rows + text),
+     or, with draft_mode="indexed", no copy: the draft reads the full cache in
+     place through the key list with svlm_decode_attn_indexed
   -> loop: gamma draft steps with svlm_decode_attn over the draft cache,
            one dense verify pass with svlm_decode_attn (gamma + 1 queries,
            causal tail) over the full cache, svlm_verify greedy acceptance,
@@ -131,6 +133,28 @@ def decode(model: TinyDecoder, tokens: torch.Tensor, cache: KVCache) -> torch.Te
     return _rms(h) @ model.w["lm"]
 
 
+def decode_draft_indexed(model: TinyDecoder, token: torch.Tensor, full: KVCache, lst: torch.Tensor,
+                         n_idx: int) -> torch.Tensor:
+    """One draft step that reads the full cache in place: the token's K/V go to
+    row full.length (the verify pass rewrites that row), and attention runs
+    with svlm_decode_attn_indexed over the first n_idx rows named by `lst`
+    (kept visual rows, then every row from the text on, this one included).
+    Returns logits [1][vocab]; full.length grows by one."""
+    p0 = full.length
+    nt = torch.tensor([n_idx], dtype=torch.int32, device=token.device)
+    h = model.w["emb"][token]
+    for l in range(model.layers):
+        a = _rms(h)
+        q = (a @ model.w[f"q{l}"]).view(1, 1, model.hq, model.d).to(torch.bfloat16)
+        full.k[l][:, p0] = (a @ model.w[f"k{l}"]).view(model.hkv, model.d).to(torch.bfloat16)
+        full.v[l][:, p0] = (a @ model.w[f"v{l}"]).view(model.hkv, model.d).to(torch.bfloat16)
+        o, _ = ops.decode_attn_indexed(q, full.k[l], full.v[l], lst, nt, False, want_lse=False)
+        h = h + o.view(1, model.hq * model.d) @ model.w[f"o{l}"]
+        h = h + torch.relu(_rms(h) @ model.w[f"up{l}"]) @ model.w[f"dn{l}"]
+    full.length = p0 + 1
+    return _rms(h) @ model.w["lm"]
+
+
 @dataclass
 class Video:
     """A prompt of F x H x W visual embeddings followed by T text tokens."""
@@ -160,9 +184,14 @@ def greedy_dense(model: TinyDecoder, video: Video, n_new: int) -> list:
     return out
 
 
-def speculative(model: TinyDecoder, video: Video, n_new: int, gamma: int, keep: float, top_p: float):
-    """Greedy speculative decoding with a pruned-KV self-draft.  Returns the
-    tokens and per-cycle accepted-draft counts."""
+def speculative(model: TinyDecoder, video: Video, n_new: int, gamma: int, keep: float, top_p: float,
+                draft_mode: str = "compact"):
+    """Greedy speculative decoding with a pruned-KV self-draft.  draft_mode
+    "compact" gathers the kept KV into a draft cache; "indexed" reads it in
+    place from the full cache through the key list.  Returns the tokens and
+    per-cycle accepted-draft counts."""
+    if draft_mode not in ("compact", "indexed"):
+        raise ValueError(f"unknown draft_mode {draft_mode!r}")
     dev = video.text.device
     T = video.text.shape[0]
     n_vis = video.n_vis
@@ -179,22 +208,33 @@ def speculative(model: TinyDecoder, video: Video, n_new: int, gamma: int, keep: 
                   alpha=1.0 / model.layers, beta=0.0 if l == 0 else 1.0, out=row)
     budget = math.ceil(keep * n_vis)
     kept, _, _ = ops.select(row, video.frames, video.gh, video.gw, top_p, budget)
-    draft = KVCache.empty(model, budget + T + n_new + gamma + 2, dev)
-    for l in range(model.layers):
-        ops.gather_kv(full.k[l][:, :N], full.v[l][:, :N], kept[0], n_vis, T,
-                      draft.k[l][:, :budget + T], draft.v[l][:, :budget + T])
-    draft.length = budget + T
+    if draft_mode == "indexed":
+        # list entry budget + j names row n_vis + j (text, then generated tokens)
+        lst = torch.cat([kept[0], torch.arange(n_vis, cap, dtype=torch.int32, device=dev)])
+    else:
+        draft = KVCache.empty(model, budget + T + n_new + gamma + 2, dev)
+        for l in range(model.layers):
+            ops.gather_kv(full.k[l][:, :N], full.v[l][:, :N], kept[0], n_vis, T,
+                          draft.k[l][:, :budget + T], draft.v[l][:, :budget + T])
+        draft.length = budget + T
 
     tok = int(logits[0].argmax())
     out = [tok]
     accepted = []
     while len(out) < n_new:
-        d0, f0 = draft.length, full.length
+        f0 = full.length
+        d0 = draft.length if draft_mode == "compact" else 0
         drafts = []
         t = tok
         for _ in range(gamma):
-            t = int(decode(model, torch.tensor([t], device=dev), draft)[0].argmax())
+            tt = torch.tensor([t], device=dev)
+            if draft_mode == "indexed":
+                lg = decode_draft_indexed(model, tt, full, lst, budget + full.length + 1 - n_vis)
+            else:
+                lg = decode(model, tt, draft)
+            t = int(lg[0].argmax())
             drafts.append(t)
+        full.length = f0          # the draft's rows are rewritten by the verify pass
         vt = torch.tensor([tok] + drafts, dtype=torch.int64, device=dev)
         lv = decode(model, vt, full)                                   # [gamma + 1][vocab]
         n_acc, nxt = ops.verify("greedy", torch.tensor([drafts], dtype=torch.int32, device=dev),
@@ -202,10 +242,11 @@ def speculative(model: TinyDecoder, video: Video, n_new: int, gamma: int, keep: 
         n = int(n_acc[0])
         # keep the verified rows (tok and the accepted drafts) in both caches
         full.length = f0 + 1 + n
-        for l in range(model.layers):
-            draft.k[l][:, d0:d0 + 1 + n] = full.k[l][:, f0:f0 + 1 + n]
-            draft.v[l][:, d0:d0 + 1 + n] = full.v[l][:, f0:f0 + 1 + n]
-        draft.length = d0 + 1 + n
+        if draft_mode == "compact":
+            for l in range(model.layers):
+                draft.k[l][:, d0:d0 + 1 + n] = full.k[l][:, f0:f0 + 1 + n]
+                draft.v[l][:, d0:d0 + 1 + n] = full.v[l][:, f0:f0 + 1 + n]
+            draft.length = d0 + 1 + n
         accepted.append(n)
         tok = int(nxt[0])
         out.extend(drafts[:n] + [tok])

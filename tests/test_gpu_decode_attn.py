@@ -61,7 +61,7 @@ def test_tiny_config_verify_and_draft():
 
 
 # every (G, nq) with every key count that holds the nq new tokens
-_SHAPES = [(G, nq, N) for G, nq in [(1, 1), (2, 5), (5, 10), (7, 1), (8, 6), (8, 1)]
+_SHAPES = [(G, nq, N) for G, nq in [(1, 1), (2, 5), (5, 10), (7, 1), (7, 10), (8, 6), (8, 1)]
            for N in [1, 31, 33, 65, 1000, 4099] if N >= nq]
 
 
@@ -174,6 +174,17 @@ def test_hour_long_shape_verify_sampled_heads():
     ro, rl = oracle.decode_attn(q[:, :, :G], k[:1], v[:1], [N], True)
     assert row_rel_err(o[:, :, :G], ro) <= TOL
     assert np.abs(lse[:, :, :G] - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("G,nq,N", [(5, 10, 20842), (7, 10, 16384), (8, 10, 17001)])
+def test_long_context_row_chunks(G, nq, N):
+    """At D = 128 and long contexts, 49-80 query rows run as one chunk of four
+    or five row blocks (merged in two groups); the 32B shape is the first case."""
+    Hkv = 2
+    q = _rand(61 + G, 1, nq, G * Hkv, 128)
+    k = _rand(62 + G, Hkv, N, 128)
+    v = _rand(63 + G, Hkv, N, 128)
+    _check(q, k, v, [N], True, name=f"long context G{G} nq{nq} N{N}")
 
 
 @pytest.mark.parametrize("scale_q", [8.0, 32.0])

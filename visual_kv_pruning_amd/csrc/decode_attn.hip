@@ -8,9 +8,10 @@
 // memory bandwidth (SpecVLM technology-transfer listing, section 4).
 //
 // Design (one wave = 64 lanes; c = lane % 16, g = lane / 16):
-//  * a workgroup owns one (batch, KV head, key split) and up to 48 query rows
-//    (80 at D = 64; rows = G * nq, row r = i * G + local head), padded to
-//    16-row MFMA blocks; four waves, one workgroup per compute unit;
+//  * a workgroup owns one (batch, KV head, key split) and up to 80 query rows
+//    (at D = 128 and short contexts 48; rows = G * nq, row r = i * G + local
+//    head), padded to 16-row MFMA blocks; four waves, one workgroup per
+//    compute unit;
 //  * wave w takes the 16-key blocks 64 j + 16 w of the split, so the waves stay
 //    balanced; it stages its own blocks HBM -> LDS with LDS-DMA transfers
 //    (range-checked buffer descriptors, nontemporal) through a private ring
@@ -66,8 +67,15 @@ constexpr int kMaxIdxSplit = 2048;
 constexpr int kWaves = 4;                  // waves per workgroup
 constexpr int kBlock = 16;                 // keys per wave per step (one MFMA block)
 constexpr int kStep = kWaves * kBlock;     // keys per workgroup step
-constexpr int kMaxRB128 = 3;               // query row blocks per workgroup at D = 128 (48 rows)
-constexpr int kMaxRB64 = 5;                // 80 rows at D = 64
+constexpr int kMaxRB = 5;                  // query row blocks per workgroup (80 rows)
+// At D = 128 a chunk of more than three row blocks (48 rows) pays for itself
+// only at long contexts: two chunks read every K and V row twice, which costs
+// HBM bandwidth once a split's keys outgrow its share of the XCD's L2, while
+// four or five row blocks make the key loop arithmetic-bound.  Measured at
+// 70 rows: 8266 keys 16.6 us in two chunks against 23.0 us in one; 141194
+// keys 90 us against 84 us.  At 50 rows and 20842 keys: 29.2 against 26.9 us.
+constexpr int kMaxRBShort = 3;
+constexpr int kLongContextKeys = 16384;
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescaleSum = 256.f;  // a lane's 4-key weight sum above this raises the row references
 
@@ -136,8 +144,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   // that wave's merge slice; per-wave row maxima and sums for the merge.
   // slots allocated per wave: the NS that cycle, or more where the wave's
   // merge slice (RP rows of OSTRIDE floats) needs the room after the loop
-  constexpr int NSA = (RP * OSTRIDE * 4 + SLOT - 1) / SLOT > NS ? (RP * OSTRIDE * 4 + SLOT - 1) / SLOT : NS;
-  static_assert((size_t)kWaves * NSA * SLOT <= 144 * 1024, "LDS");
+  // (capped at 128 KB in all; larger row chunks merge in groups of MG row blocks)
+  constexpr int NSA_WANT = (RP * OSTRIDE * 4 + SLOT - 1) / SLOT;
+  constexpr int NSA_CAP = 128 * 1024 / (kWaves * SLOT);
+  constexpr int NSA = NSA_WANT > NS ? (NSA_WANT < NSA_CAP ? NSA_WANT : NSA_CAP) : NS;
+  constexpr int MG = (NSA * SLOT / (OSTRIDE * 4)) / 16 < RB ? (NSA * SLOT / (OSTRIDE * 4)) / 16 : RB;
+  static_assert(MG >= 1 && (size_t)kWaves * NSA * SLOT <= 144 * 1024, "LDS");
   __shared__ __align__(16) unsigned char lds[(size_t)kWaves * NSA * SLOT];
   __shared__ float sm_m[kWaves][RP];
   __shared__ float sm_l[kWaves][RP];
@@ -392,75 +404,159 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   // ---- merge the waves: each parks its row maxima, row sums and unscaled
   // output sums in a slice inside its own staging ring (which only it has
   // used), so no wave waits for another before writing; after one barrier
-  // every thread weights
-  // and adds the slices of its (row, 4 columns) items in wave order and writes
-  // them with coalesced stores.  All LDS loads of a thread are issued together.
-  {
-    float* my_slice = (float*)my_ring;
+  // every thread weights and adds the slices of its (row, 4 columns) items in
+  // wave order and writes them with coalesced stores.  All LDS loads of a
+  // thread are issued together.  Up to 48 rows (three row blocks at D = 128)
+  // merge in one pass; larger chunks in groups of MG row blocks, with a
+  // barrier between groups.  (The one-pass form is kept as written for the
+  // chunks it covers: the grouped form, compiled for them, measured 1.4 us
+  // slower per dense-verify call at the 72B shape.)
+  if constexpr (MG >= RB) {
+    {
+      float* my_slice = (float*)my_ring;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        l_run[rb] = sum_xor32(sum_xor16(l_run[rb]));
+        const int row = rb * 16 + c;
+        if (g4 == 0) {
+          sm_m[wave][row] = m_use[rb];
+          sm_l[wave][row] = l_run[rb];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int mb = 0; mb < DV; mb += 4)
+            *(float4*)(my_slice + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
+                make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
+      }
+    }
+    __syncthreads();  // every wave's slice and row state are in LDS
+    constexpr int C4 = D / 4;
+    constexpr int ITEMS = (RP * C4 + 64 * kWaves - 1) / (64 * kWaves);
+    float4 part[ITEMS][kWaves];
+    float pm[ITEMS][kWaves], pl[ITEMS][kWaves];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int e = min((int)threadIdx.x + k * 64 * kWaves, RP * C4 - 1);
+      const int row = e / C4, d4 = e - row * C4;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        part[k][w] = *(const float4*)((const float*)(lds + (size_t)w * NSA * SLOT) + row * OSTRIDE + 4 * d4);
+        pm[k][w] = sm_m[w][row];
+        pl[k][w] = sm_l[w][row];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int e = threadIdx.x + k * 64 * kWaves;
+      if (e >= RP * C4) break;
+      const int row = e / C4, d4 = e - row * C4;
+      const int r = row_base + row;
+      if (r >= a.rows) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pm[k][w]);
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = (pm[k][w] == kNegInf) ? 0.f : fast_exp2(pm[k][w] - M);
+        L += f * pl[k][w];
+        acc.x += f * part[k][w].x;
+        acc.y += f * part[k][w].y;
+        acc.z += f * part[k][w].z;
+        acc.w += f * part[k][w].w;
+      }
+      const int qi = r / a.G;
+      const int hl = r - qi * a.G;
+      if (a.splits == 1) {
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;
+        const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
+        *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+      } else {
+        const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
+        *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
+        if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
+      }
+    }
+  } else {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l_run[rb] = sum_xor32(sum_xor16(l_run[rb]));
-      const int row = rb * 16 + c;
       if (g4 == 0) {
-        sm_m[wave][row] = m_use[rb];
-        sm_l[wave][row] = l_run[rb];
+        sm_m[wave][rb * 16 + c] = m_use[rb];
+        sm_l[wave][rb * 16 + c] = l_run[rb];
+      }
+    }
+    constexpr int C4 = D / 4;
+    constexpr int GROWS = MG * 16;  // rows per merge group
+    constexpr int ITEMS = (GROWS * C4 + 64 * kWaves - 1) / (64 * kWaves);
+#pragma unroll
+    for (int gb = 0; gb < RB; gb += MG) {
+      if (gb > 0) __syncthreads();  // the previous group's slices have been read
+      {
+        float* my_slice = (float*)my_ring;
+#pragma unroll
+        for (int rb = gb; rb < gb + MG && rb < RB; ++rb) {
+          const int row = (rb - gb) * 16 + c;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int mb = 0; mb < DV; mb += 4)
+              *(float4*)(my_slice + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
+                  make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
+        }
+      }
+      __syncthreads();  // every wave's slice and row state are in LDS
+      const int grows = min(GROWS, RP - gb * 16);  // rows of this group
+      float4 part[ITEMS][kWaves];
+      float pm[ITEMS][kWaves], pl[ITEMS][kWaves];
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) {
+        const int e = min((int)threadIdx.x + k * 64 * kWaves, grows * C4 - 1);
+        const int row = e / C4, d4 = e - row * C4;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          part[k][w] = *(const float4*)((const float*)(lds + (size_t)w * NSA * SLOT) + row * OSTRIDE + 4 * d4);
+          pm[k][w] = sm_m[w][gb * 16 + row];
+          pl[k][w] = sm_l[w][gb * 16 + row];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int k = 0; k < ITEMS; ++k) {
+        const int e = threadIdx.x + k * 64 * kWaves;
+        if (e >= grows * C4) break;
+        const int row = e / C4, d4 = e - row * C4;
+        const int r = row_base + gb * 16 + row;
+        if (r >= a.rows) continue;
+        float M = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < DV; mb += 4)
-          *(float4*)(my_slice + row * OSTRIDE + DV * (4 * g4 + i) + mb) =
-              make_float4(o[mb][rb][i], o[mb + 1][rb][i], o[mb + 2][rb][i], o[mb + 3][rb][i]);
-    }
-  }
-  __syncthreads();  // every wave's slice and row state are in LDS
-  constexpr int C4 = D / 4;
-  constexpr int ITEMS = (RP * C4 + 64 * kWaves - 1) / (64 * kWaves);
-  float4 part[ITEMS][kWaves];
-  float pm[ITEMS][kWaves], pl[ITEMS][kWaves];
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pm[k][w]);
+        float L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int e = min((int)threadIdx.x + k * 64 * kWaves, RP * C4 - 1);
-    const int row = e / C4, d4 = e - row * C4;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      part[k][w] = *(const float4*)((const float*)(lds + (size_t)w * NSA * SLOT) + row * OSTRIDE + 4 * d4);
-      pm[k][w] = sm_m[w][row];
-      pl[k][w] = sm_l[w][row];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int e = threadIdx.x + k * 64 * kWaves;
-    if (e >= RP * C4) break;
-    const int row = e / C4, d4 = e - row * C4;
-    const int r = row_base + row;
-    if (r >= a.rows) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, pm[k][w]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = (pm[k][w] == kNegInf) ? 0.f : fast_exp2(pm[k][w] - M);
-      L += f * pl[k][w];
-      acc.x += f * part[k][w].x;
-      acc.y += f * part[k][w].y;
-      acc.z += f * part[k][w].z;
-      acc.w += f * part[k][w].w;
-    }
-    const int qi = r / a.G;
-    const int hl = r - qi * a.G;
-    if (a.splits == 1) {
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;
-      const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
-      *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-      if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
-    } else {
-      const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
-      *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
-      if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = (pm[k][w] == kNegInf) ? 0.f : fast_exp2(pm[k][w] - M);
+          L += f * pl[k][w];
+          acc.x += f * part[k][w].x;
+          acc.y += f * part[k][w].y;
+          acc.z += f * part[k][w].z;
+          acc.w += f * part[k][w].w;
+        }
+        const int qi = r / a.G;
+        const int hl = r - qi * a.G;
+        if (a.splits == 1) {
+          const float inv = (L > 0.f) ? 1.f / L : 0.f;
+          const int64_t orow = ((int64_t)b * a.nq + qi) * a.Hq + (int64_t)h * a.G + hl;
+          *(float4*)(a.out + orow * D + 4 * d4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+          if (a.lse && d4 == 0) a.lse[orow] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+        } else {
+          const int64_t R = ((int64_t)b * a.Hkv + h) * a.rows + r;
+          *(float4*)(a.ws_o + (R * a.splits + s) * D + 4 * d4) = acc;
+          if (d4 == 0) *(float2*)(a.ws_ml + (R * a.splits + s) * 2) = make_float2(M, L);
+        }
+      }
     }
   }
 }
@@ -584,12 +680,8 @@ void launch_d(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t 
     case 1: launch_rb<D, 1>(a, batch, row_chunks, st); break;
     case 2: launch_rb<D, 2>(a, batch, row_chunks, st); break;
     case 3: launch_rb<D, 3>(a, batch, row_chunks, st); break;
-    default:
-      if constexpr (D == 64) {
-        if (rb == 4) launch_rb<D, 4>(a, batch, row_chunks, st);
-        else launch_rb<D, 5>(a, batch, row_chunks, st);
-      }
-      break;
+    case 4: launch_rb<D, 4>(a, batch, row_chunks, st); break;
+    default: launch_rb<D, 5>(a, batch, row_chunks, st); break;
   }
 }
 
@@ -605,7 +697,7 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
                int max_steps_per_split = 0) {
   Plan p;
   const int rows = (Hq / Hkv) * nq;
-  const int max_rb = (D == 128) ? kMaxRB128 : kMaxRB64;
+  const int max_rb = (D == 128 && max_kv_len < kLongContextKeys) ? kMaxRBShort : kMaxRB;
   // row blocks per chunk: as few chunks as possible, then as few padded rows
   const int chunks = (rows + max_rb * 16 - 1) / (max_rb * 16);
   p.rb = ((rows + chunks - 1) / chunks + 15) / 16;

@@ -265,6 +265,13 @@ def main():
     torch.cuda.synchronize()
     pd_us = a.elapsed_time(b) * 1e3 / args.steps     # both branches, all 80 layers
 
+    # (2c) the hour-long shape (Sparse-to-Dense explainer, "problem statement"
+    # and "KV cache selection"; Qwen2-VL-7B heads): dense verify of gamma + 1 = 10
+    # queries over 141194 keys, and the draft over per-head lists of 1024 kept
+    # visual rows + the 64 text rows + the newest row, read in place.  Reported
+    # beside the workload above, not part of `value`.
+    hour = measure_hour_shape(torch, ops, dev, g, args.steps)
+
     # (3) an achievable streaming rate on this part: a plain device copy of the
     # 80-layer K cache (read + write bytes), timed the same way
     copy_dst = torch.empty_like(K)
@@ -348,6 +355,7 @@ def main():
             "gbs": round(L * (verify_bytes + draft_bytes) / (pd_us * 1e-6) / 1e9, 1),
             "what": "80 dense-verify and 80 draft launches overlapped on two streams (one graph, two branches); "
                     "decode_attn_us_per_step runs them one after the other"},
+        "hour_shape": hour,
         "achievable": {"copy_gbs": round(copy_gbs, 1),
                        "what": "device copy of the 80-layer K cache (4.1 GB), read + write bytes per second"},
     }
@@ -355,6 +363,71 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, N_full, N_draft, bytes_row, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
+    """Verify and in-place draft attention at the hour-long shape, rotating over
+    `layers` layer buffers (2.3 GB of KV, well past the 256 MB Infinity Cache);
+    per-call times from HIP events around graph replays."""
+    c5 = W.C5
+    Hq, Hkv, D = c5.hq, c5.hkv, c5.d
+    nq = c5.gamma_verify + 1
+    N = c5.n_ctx + nq                                  # 141194 keys
+    n_draft = c5.budget + c5.n_text + 1                # 1089 keys per head
+    kv = torch.empty(2, layers, Hkv, N, D, dtype=torch.bfloat16, device=dev)
+    for l in range(layers):
+        kv[:, l].copy_(torch.randn(2, Hkv, N, D, generator=g, device=dev, dtype=torch.float32))
+    qv = torch.randn(layers, 1, nq, Hq, D, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    qd = torch.randn(layers, 1, 1, Hq, D, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    idx = torch.empty(Hkv, n_draft, dtype=torch.int32, device=dev)
+    for h in range(Hkv):
+        pick = torch.randperm(c5.n_vis, generator=g, device=dev)[:c5.budget]
+        idx[h, :c5.budget] = torch.sort(pick).values.to(torch.int32)
+        idx[h, c5.budget:] = torch.arange(c5.n_vis, c5.n_vis + c5.n_text + 1, dtype=torch.int32, device=dev)
+    len_v = torch.tensor([N], dtype=torch.int32, device=dev)
+    len_d = torch.tensor([n_draft], dtype=torch.int32, device=dev)
+    ws_v = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, nq, Hq, Hkv, D, N)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(256, ops.decode_attn_indexed_workspace_bytes(1, 1, Hq, Hkv, D, n_draft)),
+                       dtype=torch.uint8, device=dev)
+    o_v = torch.empty(1, nq, Hq, D, dtype=torch.float32, device=dev)
+    l_v = torch.empty(1, nq, Hq, dtype=torch.float32, device=dev)
+    o_d = torch.empty(1, 1, Hq, D, dtype=torch.float32, device=dev)
+    l_d = torch.empty(1, 1, Hq, dtype=torch.float32, device=dev)
+
+    def verify():
+        for l in range(layers):
+            ops.decode_attn(qv[l], kv[0, l], kv[1, l], len_v, True, out=o_v, lse=l_v, ws=ws_v)
+
+    def draft():
+        for l in range(layers):
+            ops.decode_attn_indexed(qd[l], kv[0, l], kv[1, l], idx, len_d, False, out=o_d, lse=l_d, ws=ws_d)
+
+    out = {}
+    row = Hkv * D * 2 * 2
+    for name, fn, nbytes in (("verify_attn", verify, N * row), ("draft_attn_indexed", draft, n_draft * row)):
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (steps * layers)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us_avg": round(us, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["verify_attn"]["what"] = "dense verify, 10 queries x 141194 keys, 28 q / 4 KV heads, D 128"
+    out["draft_attn_indexed"]["what"] = ("draft, 1 query over per-head lists of 1024 visual + 64 text + 1 rows "
+                                         "read in place")
+    del kv
+    return out
 
 
 def cpu_baseline(cfg, N_full, N_draft, bytes_row, budget_s):

@@ -22,10 +22,11 @@
 //    cross-lane steps (v_permlane16/32_swap);
 //  * online softmax in the exp2 domain with a lazy rescale (the reference
 //    maximum moves only when a block exceeds it by more than 2^8);
-//  * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: the scores already sit in the
-//    B-operand layout; P enters as a bf16 hi + lo pair (two products), so the
-//    weights carry ~2^-16 relative error; V^T operands come from 16-byte V
-//    rows by byte permutes;
+//  * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16: the scores already sit in the
+//    B-operand layout; P enters as bf16 hi + lo halves in the two halves of
+//    the contraction (the V operand repeated), so the weights carry ~2^-16
+//    relative error at the cost of one instruction; V^T operands come from
+//    16-byte V rows by byte permutes;
 //  * the four waves merge through LDS in a fixed order, then the workgroup
 //    writes either the final fp32 output (one split) or a partial (max, sum,
 //    output) that a second kernel merges in split order.  Deterministic.
@@ -360,37 +361,40 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
         s4[rb] = (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
       }
     }
-    // P^T as the B operand of the 16x16x16 product: lane (c, g4) holds
-    // P[row c][keys 4 g4 .. 4 g4 + 3] exactly where the scores are; bf16 hi + lo
-    bf16x4 phi[RB], plo[RB];
+    // P^T as the B operand of the V product: lane (c, g4) holds
+    // P[row c][keys 4 g4 .. 4 g4 + 3] exactly where the scores are, as bf16
+    // hi + lo halves: the lane's eight contraction slots of one
+    // v_mfma_f32_16x16x32_bf16 take the four hi halves, then the four lo
+    // halves, and the A operand repeats the same four V values in both, so one
+    // instruction (issuing at the rate of the 16x16x16 form) adds V (hi + lo)
+    bf16x8 pp[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l_run[rb] += s4[rb];
-      u32x2 hi, lo;
+      u32x4 hl;
 #pragma unroll
       for (int qd = 0; qd < 2; ++qd) {
         const unsigned b0 = f_bits(p[rb][2 * qd]), b1 = f_bits(p[rb][2 * qd + 1]);
-        hi[qd] = perm(b1, b0, kPermHi);
+        hl[qd] = perm(b1, b0, kPermHi);
         const float r0 = p[rb][2 * qd] - bits_f(b0 & 0xFFFF0000u);
         const float r1 = p[rb][2 * qd + 1] - bits_f(b1 & 0xFFFF0000u);
-        lo[qd] = perm(f_bits(r1), f_bits(r0), kPermHi);
+        hl[2 + qd] = perm(f_bits(r1), f_bits(r0), kPermHi);
       }
-      phi[rb] = as_bf16x4(hi);
-      plo[rb] = as_bf16x4(lo);
+      pp[rb] = as_bf16x8(hl);
     }
-    // O^T += V^T P^T: the A operand of d-block mb holds V[keys 4 g4 .. + 3][d = DV c + mb]
+    // O^T += V^T P^T: the A operand of d-block mb holds V[keys 4 g4 .. + 3][d = DV c + mb], twice
 #pragma unroll
     for (int mb = 0; mb < DV; ++mb) {
       const int w = mb >> 1;
       const unsigned sel = (mb & 1) ? kPermHi : kPermLo;
-      u32x2 vv;
+      u32x4 vv;
       vv[0] = perm(vt[1][w], vt[0][w], sel);
       vv[1] = perm(vt[3][w], vt[2][w], sel);
-      const bf16x4 vop = as_bf16x4(vv);
+      vv[2] = vv[0];
+      vv[3] = vv[1];
+      const bf16x8 vop = as_bf16x8(vv);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16k16(vop, phi[rb], o[mb][rb]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16k16(vop, plo[rb], o[mb][rb]);
+      for (int rb = 0; rb < RB; ++rb) o[mb][rb] = mfma16(vop, pp[rb], o[mb][rb]);
     }
   };
   // blocks below n_full see every key of every row

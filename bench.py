@@ -367,8 +367,9 @@ def main():
 
 def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
     """Verify and in-place draft attention at the hour-long shape, rotating over
-    `layers` layer buffers (2.3 GB of KV, well past the 256 MB Infinity Cache);
-    per-call times from HIP events around graph replays."""
+    `layers` layer buffers (2.3 GB of KV, well past the 256 MB Infinity Cache),
+    and the per-(layer, KV head) top-K selection; per-call times from HIP
+    events around graph replays."""
     c5 = W.C5
     Hq, Hkv, D = c5.hq, c5.hkv, c5.d
     nq = c5.gamma_verify + 1
@@ -402,9 +403,21 @@ def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
         for l in range(layers):
             ops.decode_attn_indexed(qd[l], kv[0, l], kv[1, l], idx, len_d, False, out=o_d, lse=l_d, ws=ws_d)
 
+    # selection at this shape: one row per (layer, KV head), 28 x 4 = 112 rows of
+    # 141120 scores, pure top-K = 1024 (Sparse-to-Dense explainer, "KV cache
+    # selection"); heavy-tailed synthetic rows, each summing to 1
+    R = c5.layers * Hkv
+    srows = torch.rand(R, c5.n_vis, generator=g, device=dev, dtype=torch.float32).pow_(8.0)
+    srows.div_(srows.sum(dim=1, keepdim=True))
+
+    def select():
+        ops.select(srows, c5.frames, c5.gh, c5.gw, c5.top_p, c5.budget)
+
     out = {}
     row = Hkv * D * 2 * 2
-    for name, fn, nbytes in (("verify_attn", verify, N * row), ("draft_attn_indexed", draft, n_draft * row)):
+    for name, fn, nbytes, n_calls in (("verify_attn", verify, N * row, layers),
+                                      ("draft_attn_indexed", draft, n_draft * row, layers),
+                                      ("select", select, R * (c5.n_vis + c5.budget) * 4, 1)):
         fn()
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
@@ -419,10 +432,12 @@ def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
             gr.replay()
         b.record()
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (steps * layers)
+        us = a.elapsed_time(b) * 1e3 / (steps * n_calls)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us_avg": round(us, 3), "bytes": nbytes, "gbs": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["select"]["what"] = ("112 rows (28 layers x 4 KV heads) x 141120 scores, top-K 1024; bytes = scores read "
+                             "once + indices written")
     out["verify_attn"]["what"] = "dense verify, 10 queries x 141194 keys, 28 q / 4 KV heads, D 128"
     out["draft_attn_indexed"]["what"] = ("draft, 1 query over per-head lists of 1024 visual + 64 text + 1 rows "
                                          "read in place")

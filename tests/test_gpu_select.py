@@ -46,6 +46,26 @@ def test_budget_edges(budget):
     _check(rows, F, H, Wd, 0.5, budget, f"budget={budget}")
 
 
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+@pytest.mark.parametrize("top_p", [0.0, 0.5, 1.0])
+def test_long_rows_chunked(kind, top_p):
+    """Rows past the register-resident limit (32768 tokens) are taken in chunks
+    of 16384 tokens with the ordered scans carried across them; 50 frames of
+    28 x 28 = 39200 tokens end in a partial chunk."""
+    F, H, Wd = 50, 28, 28
+    N = F * H * Wd
+    rows = W.score_rows(kind, 2, N, seed=11)
+    _check(rows, F, H, Wd, top_p, int(math.ceil(0.1 * N)), f"long {kind}")
+
+
+@pytest.mark.parametrize("budget", [0, 1, 16383, 16384, 16385, 39199, 39200])
+def test_long_rows_budget_edges(budget):
+    """Budgets at the chunk boundary and at the row length on the chunked path."""
+    F, H, Wd = 50, 28, 28
+    rows = W.score_rows("lognormal2", 1, F * H * Wd, seed=12)
+    _check(rows, F, H, Wd, 0.5, budget, f"long budget={budget}")
+
+
 def test_golden_worked_example():
     s = np.array([4, 0, 1, 8, 2, 2, 0, 3, 16, 1, 2, 1], np.float32) / np.float32(64)
     for p, b in ((0.5, 5), (0.9, 5), (0.0, 4), (1.0, 4), (0.3, 5)):

@@ -28,6 +28,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRegKeys = 32;  // keys per thread held in registers (rows up to 32768 tokens)
+constexpr int kChunkRunKeys = 16;  // keys per thread per chunk for longer rows (fits 128 VGPRs)
 constexpr int kCopies = 32;
 constexpr int kCntStride = 257;   // words
 constexpr int kMassStride = 257;  // 8-byte words
@@ -59,8 +60,8 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 }
 
 // block-wide exclusive scan (thread order) of two counters packed in 64 bits
-// (each part < 2^32; tokens per row < 2^18)
-__device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm) {
+// (each part < 2^32; tokens per row < 2^18); *total gets the block's sum
+__device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm, uint64_t* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint64_t incl = x;
 #pragma unroll
@@ -70,17 +71,28 @@ __device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm) {
   }
   if (lane == 63) sm[wv] = incl;
   __syncthreads();
-  uint64_t before = 0;
+  uint64_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w)
+  for (int w = 0; w < kWaves; ++w) {
     if (w < wv) before += sm[w];
+    all += sm[w];
+  }
+  *total = all;
   return before + incl - x;
 }
 
-// KREG > 0: the thread's run of keys lives in registers; KREG == 0: it is read
-// from memory on every pass
-template <int KREG>
+// Rows of up to kThreads * kRegKeys tokens: each thread's run of tokens lives
+// in registers for the whole kernel.  Longer rows (CHUNKED): the row is taken
+// in chunks of kThreads * kChunkRunKeys tokens, thread t owning the run of
+// kChunkRunKeys tokens at chunk offset t * kChunkRunKeys; every pass loads a chunk's run into
+// registers (all loads of a run issued together) and the ordered scans carry
+// their totals from chunk to chunk, so raster order and exactness are those
+// of the one-chunk case.
+// MASS: the row has a Top-P stage I (0 < top_p < 1), so per-token masses are
+// summed; pure top-K and fill-only selections count tokens alone.
+template <bool CHUNKED, bool MASS>
 __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
+  constexpr int KREG = CHUNKED ? kChunkRunKeys : kRegKeys;
   // kCopies histogram copies, lane l adding to copy l % kCopies, so that at
   // most 64 / kCopies lanes of a wave meet on one counter (scores cluster in
   // a few exponents, and a shared counter serialises every lane on it); the
@@ -99,31 +111,35 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* srow = a.scores + (int64_t)row * a.row_stride;
   const int N = a.N, B = a.budget;
-  // this thread's run of tokens: [n_begin, n_begin + n_mine)
-  const int per = (N + kThreads - 1) / kThreads;
-  const int n_begin = min(N, tid * per);
-  const int n_mine = min(per, N - n_begin);
+  constexpr int kChunk = kThreads * KREG;
+  const int n_chunks = CHUNKED ? (N + kChunk - 1) / kChunk : 1;
+  // this thread's run of tokens (in the current chunk): [n_begin, n_begin + n_mine)
+  const int per = CHUNKED ? KREG : (N + kThreads - 1) / kThreads;
+  int n_begin = min(N, tid * per);
+  int n_mine = min(per, N - n_begin);
 
-  unsigned keys[KREG > 0 ? KREG : 1];
-  if constexpr (KREG > 0) {
+  unsigned keys[KREG];
+  auto load_run = [&](int ch) {
+    if constexpr (CHUNKED) {
+      n_begin = min(N, ch * kChunk + tid * KREG);
+      n_mine = max(0, min(KREG, N - n_begin));
+    }
 #pragma unroll
     for (int e = 0; e < KREG; ++e) keys[e] = key_of(srow[min(n_begin + e, N - 1)]);  // loads first, unconditional
 #pragma unroll
     for (int e = 0; e < KREG; ++e) keys[e] = (e < n_mine) ? keys[e] : 0u;
-  }
-  auto key_at = [&](int e) -> unsigned {
-    if constexpr (KREG > 0) return keys[e];
-    else return key_of(srow[n_begin + e]);
   };
+  if constexpr (!CHUNKED) load_run(0);
 
   // ---- total fixed-point mass of the row
   uint64_t q = 0;
-  if constexpr (KREG > 0) {
+  if constexpr (MASS) {
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      if constexpr (CHUNKED) load_run(ch);
 #pragma unroll
-    for (int e = 0; e < KREG; ++e)
-      if (e < n_mine) q += mass_of_key(keys[e]);
-  } else {
-    for (int n = tid; n < N; n += kThreads) q += mass_of_key(key_of(srow[n]));
+      for (int e = 0; e < KREG; ++e)
+        if (e < n_mine) q += mass_of_key(keys[e]);
+    }
   }
   q = wave_sum64(q);
   if (lane == 0) sm_q[wv] = q;
@@ -160,15 +176,14 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
         if (level == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
           const unsigned bin = (key >> shift) & 255u;
           atomicAdd(&my_cnt[bin], 1u);
-          atomicAdd(&my_mass[bin], (unsigned long long)mass_of_key(key));
+          if constexpr (MASS) atomicAdd(&my_mass[bin], (unsigned long long)mass_of_key(key));
         }
       };
-      if constexpr (KREG > 0) {
+      for (int ch = 0; ch < n_chunks; ++ch) {
+        if constexpr (CHUNKED) load_run(ch);
 #pragma unroll
         for (int e = 0; e < KREG; ++e)
           if (e < n_mine) bin_key(keys[e]);
-      } else {
-        for (int n = tid; n < N; n += kThreads) bin_key(key_of(srow[n]));
       }
       __syncthreads();
       // one thread per bin adds up the copies and clears them for the next level
@@ -256,95 +271,94 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
     k1 = (int)cnt_above + c;
   }
 
-  // ---- stage-I ranks: one ordered scan of (keys above vstar, ties at vstar)
-  unsigned my_above = 0, my_ties = 0;
-  if (k1 > 0) {
-    if constexpr (KREG > 0) {
+  // ---- stage-I ranks: one ordered scan per chunk of (keys above vstar,
+  // ties at vstar), carried across the chunks
+  const int n_rem = N - k1;
+  const int m_fill = B - k1;
+  const unsigned two_m = 2u * (unsigned)max(m_fill, 1);
+  const unsigned step_q = (unsigned)(2 * n_rem) / two_m, step_r = (unsigned)(2 * n_rem) % two_m;
+  int32_t* const kept_row = a.kept + (int64_t)row * B;
+  uint8_t* const tag_row = a.tag ? a.tag + (int64_t)row * N : nullptr;
+  unsigned carry_above = 0, carry_ties = 0;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    if constexpr (CHUNKED) {
+      if (ch > 0) __syncthreads();  // the previous chunk's scan totals have been read
+      load_run(ch);
+    }
+    unsigned my_above = 0, my_ties = 0;
+    if (k1 > 0) {
 #pragma unroll
       for (int e = 0; e < KREG; ++e)
         if (e < n_mine) {
           my_above += keys[e] > vstar ? 1u : 0u;
           my_ties += keys[e] == vstar ? 1u : 0u;
         }
-    } else {
-      for (int e = 0; e < n_mine; ++e) {
-        const unsigned key = key_at(e);
-        my_above += key > vstar ? 1u : 0u;
-        my_ties += key == vstar ? 1u : 0u;
+    }
+    uint64_t chunk_total;
+    const uint64_t before = block_excl_scan64(((uint64_t)my_ties << 32) | my_above, sm_scan, &chunk_total);
+    const unsigned above_before = carry_above + (unsigned)before;
+    unsigned ties_before = carry_ties + (unsigned)(before >> 32);
+    carry_above += (unsigned)chunk_total;
+    carry_ties += (unsigned)(chunk_total >> 32);
+
+    // ---- flags and output positions, token by token in raster order.
+    // Stage-I tokens before n: above_before + min(c_ties, ties_before).  A
+    // remainder token's rank is rho = n - that; stage II keeps the ranks
+    // floor((2j+1) n_rem / (2m)), j < m, and the picks at ranks below rho
+    // number min(m, ceil((2 m rho - n_rem) / (2 n_rem))).  The thread finds
+    // its first pending pick with one division and steps to the next ones by
+    // adding n_rem / m with a carried remainder.
+    unsigned s1_before = above_before + min(ties_before, (unsigned)c_ties);
+    int rho = n_begin - (int)s1_before;
+    int pb = 0;              // stage-II picks at ranks below rho
+    unsigned next_q = ~0u;   // rank of pick pb (none when pb == m)
+    unsigned next_r = 0;     // (2 pb + 1) n_rem mod 2m
+    if (m_fill > 0) {
+      const int64_t num = 2 * (int64_t)m_fill * rho - n_rem;
+      int64_t j = (num <= 0) ? 0 : (num + 2 * (int64_t)n_rem - 1) / (2 * (int64_t)n_rem);
+      pb = (int)(j < m_fill ? j : m_fill);
+      if (pb < m_fill) {
+        const uint64_t t = (uint64_t)(2 * pb + 1) * (uint64_t)n_rem;
+        next_q = (unsigned)(t / two_m);
+        next_r = (unsigned)(t % two_m);
       }
     }
-  }
-  const uint64_t before = block_excl_scan64(((uint64_t)my_ties << 32) | my_above, sm_scan);
-  const unsigned above_before = (unsigned)before;
-  unsigned ties_before = (unsigned)(before >> 32);
-
-  // ---- flags and output positions, token by token in raster order.  Stage-I
-  // tokens before n: above_before + min(c_ties, ties_before).  A remainder
-  // token's rank is rho = n - that; stage II keeps the ranks
-  // floor((2j+1) n_rem / (2m)), j < m, and the picks at ranks below rho number
-  // min(m, ceil((2 m rho - n_rem) / (2 n_rem))).  The thread finds its first
-  // pending pick with one division and steps to the next ones by adding
-  // n_rem / m with a carried remainder.
-  const int n_rem = N - k1;
-  const int m_fill = B - k1;
-  const unsigned two_m = 2u * (unsigned)max(m_fill, 1);
-  unsigned s1_before = above_before + min(ties_before, (unsigned)c_ties);
-  int rho = n_begin - (int)s1_before;
-  int pb = 0;              // stage-II picks at ranks below rho
-  unsigned next_q = ~0u;   // rank of pick pb (none when pb == m)
-  unsigned next_r = 0;     // (2 pb + 1) n_rem mod 2m
-  const unsigned step_q = (unsigned)(2 * n_rem) / two_m, step_r = (unsigned)(2 * n_rem) % two_m;
-  if (m_fill > 0) {
-    const int64_t num = 2 * (int64_t)m_fill * rho - n_rem;
-    int64_t j = (num <= 0) ? 0 : (num + 2 * (int64_t)n_rem - 1) / (2 * (int64_t)n_rem);
-    pb = (int)(j < m_fill ? j : m_fill);
-    if (pb < m_fill) {
-      const uint64_t t = (uint64_t)(2 * pb + 1) * (uint64_t)n_rem;
-      next_q = (unsigned)(t / two_m);
-      next_r = (unsigned)(t % two_m);
-    }
-  }
-  int32_t* const kept_row = a.kept + (int64_t)row * B;
-  uint8_t* const tag_row = a.tag ? a.tag + (int64_t)row * N : nullptr;
-  auto emit = [&](int e, unsigned key) {
-    const int n = n_begin + e;
-    const bool is_above = (k1 > 0) && key > vstar;
-    const bool is_tie = (k1 > 0) && key == vstar;
-    const bool s1 = is_above || (is_tie && ties_before < (unsigned)c_ties);
-    uint8_t tg = 0;
-    if (s1) {
-      tg = 1;
-      kept_row[s1_before + pb] = n;
-    } else {
-      if ((unsigned)rho == next_q) {
-        tg = 2;
+    auto emit = [&](int e, unsigned key) {
+      const int n = n_begin + e;
+      const bool is_above = (k1 > 0) && key > vstar;
+      const bool is_tie = (k1 > 0) && key == vstar;
+      const bool s1 = is_above || (is_tie && ties_before < (unsigned)c_ties);
+      uint8_t tg = 0;
+      if (s1) {
+        tg = 1;
         kept_row[s1_before + pb] = n;
-        ++pb;
-        if (pb < m_fill) {
-          next_q += step_q;
-          next_r += step_r;
-          if (next_r >= two_m) {
-            next_r -= two_m;
-            ++next_q;
+      } else {
+        if ((unsigned)rho == next_q) {
+          tg = 2;
+          kept_row[s1_before + pb] = n;
+          ++pb;
+          if (pb < m_fill) {
+            next_q += step_q;
+            next_r += step_r;
+            if (next_r >= two_m) {
+              next_r -= two_m;
+              ++next_q;
+            }
+          } else {
+            next_q = ~0u;
           }
-        } else {
-          next_q = ~0u;
         }
       }
-    }
-    // counters advance arithmetically (a branch on which one to bump makes the
-    // compiler address them through memory)
-    s1_before += s1 ? 1u : 0u;
-    rho += s1 ? 0 : 1;
-    if (tag_row) tag_row[n] = tg;
-    ties_before += is_tie ? 1u : 0u;
-  };
-  if constexpr (KREG > 0) {
+      // counters advance arithmetically (a branch on which one to bump makes the
+      // compiler address them through memory)
+      s1_before += s1 ? 1u : 0u;
+      rho += s1 ? 0 : 1;
+      if (tag_row) tag_row[n] = tg;
+      ties_before += is_tie ? 1u : 0u;
+    };
 #pragma unroll
     for (int e = 0; e < KREG; ++e)
       if (e < n_mine) emit(e, keys[e]);
-  } else {
-    for (int e = 0; e < n_mine; ++e) emit(e, key_at(e));
   }
   if (tid == 0) a.n_stage1[row] = k1;
 }
@@ -382,7 +396,15 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   a.kept = kept;
   a.n_stage1 = n_stage1;
   a.tag = tag;
-  if (N <= (int64_t)kThreads * kRegKeys) select_rows<kRegKeys><<<R, kThreads, 0, (hipStream_t)stream>>>(a);
-  else select_rows<0><<<R, kThreads, 0, (hipStream_t)stream>>>(a);
+  const bool mass = top_p > 0.0 && top_p < 1.0;
+  const bool chunked = N > (int64_t)kThreads * kRegKeys;
+  hipStream_t st = (hipStream_t)stream;
+  if (chunked) {
+    if (mass) select_rows<true, true><<<R, kThreads, 0, st>>>(a);
+    else select_rows<true, false><<<R, kThreads, 0, st>>>(a);
+  } else {
+    if (mass) select_rows<false, true><<<R, kThreads, 0, st>>>(a);
+    else select_rows<false, false><<<R, kThreads, 0, st>>>(a);
+  }
   return check_launch("svlm_select");
 }

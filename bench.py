@@ -284,6 +284,15 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * K.numel() * K.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
     del copy_dst
+    # and a read-only pass: torch's sum over the same 4.1 GB (reads; a few bytes written)
+    K.sum(dtype=torch.float32)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    K.sum(dtype=torch.float32)
+    b.record()
+    torch.cuda.synchronize()
+    read_gbs = K.numel() * K.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
 
     bytes_row = Hkv * D * 2 * 2                       # K + V bytes per key
     verify_bytes = N_full * bytes_row                 # per layer
@@ -356,8 +365,9 @@ def main():
             "what": "80 dense-verify and 80 draft launches overlapped on two streams (one graph, two branches); "
                     "decode_attn_us_per_step runs them one after the other"},
         "hour_shape": hour,
-        "achievable": {"copy_gbs": round(copy_gbs, 1),
-                       "what": "device copy of the 80-layer K cache (4.1 GB), read + write bytes per second"},
+        "achievable": {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
+                       "what": "device copy of the 80-layer K cache (4.1 GB), read + write bytes per second; "
+                               "torch sum over it, bytes read per second"},
     }
 
     if not args.no_cpu_baseline:

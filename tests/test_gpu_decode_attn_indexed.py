@@ -127,3 +127,17 @@ def test_bit_equal_to_gather_then_attend(nq):
     o2, l2 = ops.decode_attn_indexed(q, k, v, idx, ni, nq > 1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_hour_long_per_head_lists_full_size():
+    """The hour-long shape's in-place draft at full size: per-head lists of
+    1024 kept visual rows + the 64 text rows + the newest row, read from a
+    141194-row cache (28 q / 4 KV heads); the launch the bench times."""
+    cfg = W.C5
+    rows = cfg.n_ctx + 1
+    n_keep, tail = cfg.budget, cfg.n_text + 1
+    k, v = W.random_kv(cfg.index, cfg.hkv, rows, cfg.d, layer=3)
+    q = W.decode_queries(cfg, 3, 1)
+    lists = np.stack([_list(70 + h, rows, n_keep, tail) for h in range(cfg.hkv)])
+    _check(q, k[None], v[None], torch.tensor(lists, device="cuda:0"), lists[None], [lists.shape[1]], False,
+           "hour-long per-head lists, full size")

@@ -141,3 +141,16 @@ def test_hour_long_per_head_lists_full_size():
     lists = np.stack([_list(70 + h, rows, n_keep, tail) for h in range(cfg.hkv)])
     _check(q, k[None], v[None], torch.tensor(lists, device="cuda:0"), lists[None], [lists.shape[1]], False,
            "hour-long per-head lists, full size")
+
+
+@pytest.mark.parametrize("G,nq,n_list", [(7, 10, 17000), (5, 10, 16500)])
+def test_long_list_five_and_four_row_blocks(G, nq, n_list):
+    """Lists of at least 16384 keys with 50-80 query rows run as one chunk of
+    four or five row blocks through the index list (the long-context path)."""
+    Hkv, D, rows = 2, 128, 20000
+    q = _rand(81 + G, 1, nq, G * Hkv, D)
+    k = _rand(82 + G, 1, Hkv, rows, D)
+    v = _rand(83 + G, 1, Hkv, rows, D)
+    lists = np.stack([_list(84 + G + h, rows, n_list - 64, 64) for h in range(Hkv)])
+    _check(q, k, v, torch.tensor(lists, device="cuda:0"), lists[None], [lists.shape[1]], True,
+           f"long list G{G} nq{nq} n{n_list}")

@@ -127,6 +127,8 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     assert lib.svlm_select(fake, 1 << 20, 1, 1024, 16, 17, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_UNSUPPORTED
     assert lib.svlm_select(fake, 20, 1, 2, 2, 5, float("nan"), 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID
     assert lib.svlm_select(fake, 10, 1, 2, 2, 5, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID  # stride
+    # select with no rows is a no-op (nothing is launched, pointers may be null)
+    assert lib.svlm_select(NULL, 20, 0, 2, 2, 5, 0.5, 2, NULL, NULL, NULL, NULL, 0, NULL) == L.SVLM_OK
     # gather: tail past the source, unsupported D
     assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 8, 3, fake, fake, 0, 128, 1, 128, 0, NULL) == L.SVLM_E_INVALID
     assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 0, 3, fake, fake, 0, 128, 1, 80, 0, NULL) == L.SVLM_E_UNSUPPORTED

@@ -112,3 +112,41 @@ def test_wide_score_range():
     p = dataclasses.replace(p, q_text=p.q_text * 4.0)
     log("score case wide score range")
     _compare(_gpu_score(p, cfg, "kvhead"), _ref(p, cfg, "kvhead"), "C2 q x4")
+
+
+@dataclasses.dataclass
+class _Layer:
+    q_text: np.ndarray
+    k: np.ndarray
+    q_pos0: int
+
+
+@dataclasses.dataclass
+class _Shape:
+    n_vis: int
+    hkv: int
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,n_vis,pre,post,Hq,Hkv", [
+    (1, 1, 0, 0, 2, 2),        # one text query, one visual token
+    (1, 300, 5, 3, 4, 1),      # one query; keys before and after the visual window
+    (17, 63, 0, 0, 6, 2),      # ragged text rows and keys (not multiples of 16 or 64)
+    (33, 1000, 12, 40, 8, 8),  # MHA (one head per group), visual window inside the context
+    (128, 129, 1, 0, 16, 2),   # a full 128-row block of text queries
+])
+def test_edge_shapes(D, T, n_vis, pre, post, Hq, Hkv):
+    """Edge shapes vs the oracle: single query and single visual token, ragged
+    text rows and key counts, keys before the visual window (vis_start > 0)
+    and text tokens between it and the queries."""
+    rng = np.random.default_rng(D * 1000 + T * 7 + n_vis)
+    q_pos0 = pre + n_vis + post
+    n_ctx = q_pos0 + T
+    q = W.bf16_round(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    k = W.bf16_round(rng.standard_normal((Hkv, n_ctx, D)).astype(np.float32))
+    p = _Layer(q, k, q_pos0)
+    shape = _Shape(n_vis, Hkv)
+    log(f"score case edge D{D} T{T} n_vis{n_vis} pre{pre} post{post} Hq{Hq} Hkv{Hkv}")
+    for agg in ("qhead", "kvhead", "all"):
+        _compare(_gpu_score(p, shape, agg, n_vis=n_vis, vis_start=pre), _ref(p, shape, agg, n_vis, pre),
+                 f"edge {agg}")

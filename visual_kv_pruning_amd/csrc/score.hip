@@ -98,10 +98,15 @@ struct KRing {
   static constexpr int PW = NI / W;
   static_assert(PW >= 1 && NI % W == 0, "tile transfers must split evenly over the waves");
   static_assert((NS - 1) * PW <= 63, "ring depth");
+  static constexpr int kMaxPW = 16;  // one wave staging a whole D = 128 tile
+  static_assert(PW <= kMaxPW, "transfers per wave");
   __amdgpu_buffer_rsrc_t rs;
   unsigned char* lds;
   int wave, row_bytes;
-  int src_lane[4] = {0, 0, 0, 0};
+  // per-lane source offset of each of this wave's PW transfers (set by init;
+  // a fixed bound: sized by PW, the host pass of this compiler dropped the
+  // kernels' launch stubs)
+  int src_lane[kMaxPW];
 
   __device__ void init(const uint16_t* k_rows, int n_rows, int64_t k_sn, unsigned char* ring, int w) {
     const int lane = threadIdx.x & 63;

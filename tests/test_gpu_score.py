@@ -134,6 +134,7 @@ class _Shape:
     (17, 63, 0, 0, 6, 2),      # ragged text rows and keys (not multiples of 16 or 64)
     (33, 1000, 12, 40, 8, 8),  # MHA (one head per group), visual window inside the context
     (128, 129, 1, 0, 16, 2),   # a full 128-row block of text queries
+    (20, 500, 0, 8, 32, 2),    # 16 q heads per KV head (two head groups in both passes)
 ])
 def test_edge_shapes(D, T, n_vis, pre, post, Hq, Hkv):
     """Edge shapes vs the oracle: single query and single visual token, ragged

@@ -66,6 +66,25 @@ def test_long_rows_budget_edges(budget):
     _check(rows, F, H, Wd, 0.5, budget, f"long budget={budget}")
 
 
+def test_strided_rows():
+    """Rows taken from a wider matrix (row stride > F*H*W), as from a slice."""
+    from visual_kv_pruning_amd import ops
+    F, H, Wd = 4, 7, 9
+    N = F * H * Wd
+    rows = W.score_rows("lognormal2", 5, N, seed=13)
+    wide = np.zeros((5, N + 37), np.float32)
+    wide[:, :N] = rows
+    wide[:, N:] = 1.0                      # never read: past each row
+    log("select case strided rows")
+    s = torch.from_numpy(wide).to("cuda:0")[:, :N]
+    kept, n1, tag = ops.select(s, F, H, Wd, 0.5, 25, with_tag=True)
+    torch.cuda.synchronize()
+    rk, r1, rt = oracle.select_rows(rows, F, H, Wd, 0.5, 25)
+    assert np.array_equal(n1.cpu().numpy(), r1)
+    assert np.array_equal(kept.cpu().numpy(), rk.astype(np.int32))
+    assert np.array_equal(tag.cpu().numpy(), rt)
+
+
 def test_golden_worked_example():
     s = np.array([4, 0, 1, 8, 2, 2, 0, 3, 16, 1, 2, 1], np.float32) / np.float32(64)
     for p, b in ((0.5, 5), (0.9, 5), (0.0, 4), (1.0, 4), (0.3, 5)):

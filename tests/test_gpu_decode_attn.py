@@ -61,7 +61,7 @@ def test_tiny_config_verify_and_draft():
 
 
 # every (G, nq) with every key count that holds the nq new tokens
-_SHAPES = [(G, nq, N) for G, nq in [(1, 1), (2, 5), (5, 10), (7, 1), (7, 10), (8, 6), (8, 1)]
+_SHAPES = [(G, nq, N) for G, nq in [(1, 1), (2, 5), (5, 10), (7, 1), (7, 10), (8, 6), (8, 1), (16, 6)]
            for N in [1, 31, 33, 65, 1000, 4099] if N >= nq]
 
 
@@ -176,10 +176,11 @@ def test_hour_long_shape_verify_sampled_heads():
     assert np.abs(lse[:, :, :G] - rl).max() <= 1e-3
 
 
-@pytest.mark.parametrize("G,nq,N", [(5, 10, 20842), (7, 10, 16384), (8, 10, 17001)])
+@pytest.mark.parametrize("G,nq,N", [(5, 10, 20842), (7, 10, 16384), (8, 10, 17001), (16, 6, 16500)])
 def test_long_context_row_chunks(G, nq, N):
     """At D = 128 and long contexts, 49-80 query rows run as one chunk of four
-    or five row blocks (merged in two groups); the 32B shape is the first case."""
+    or five row blocks (merged in two groups); the 32B shape is the first case.
+    96 rows need two chunks even there."""
     Hkv = 2
     q = _rand(61 + G, 1, nq, G * Hkv, 128)
     k = _rand(62 + G, Hkv, N, 128)

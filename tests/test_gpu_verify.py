@@ -77,3 +77,34 @@ def test_reject_special_cases():
     n, t = _gpu("reject", np.array([[0]]), pz, qz, np.array([[0.5, 0.5]], np.float32))
     rn, rt = oracle.verify_reject(np.array([[0]]), pz, qz, np.array([[0.5, 0.5]], np.float32))
     assert (n[0], t[0]) == (rn[0], rt[0]) == (0, 3)
+
+
+@pytest.mark.parametrize("first_miss", [None, 0, 63, 64, 66, 69])
+def test_long_windows_cross_the_64_position_rounds(first_miss):
+    """gamma = 70 drafted tokens: the first mismatch (or rejection) is searched
+    64 positions at a time; drafts agree with the target up to `first_miss`
+    (None: all accepted, the bonus token comes from the last row)."""
+    gamma, V, B = 70, 300, 2
+    rng = np.random.default_rng(99 if first_miss is None else first_miss)
+    logits = rng.standard_normal((B, gamma + 1, V)).astype(np.float32)
+    d = logits[:, :gamma].argmax(-1).astype(np.int32)
+    if first_miss is not None:
+        d[:, first_miss] = (d[:, first_miss] + 1) % V
+    log(f"verify case long window greedy first_miss={first_miss}")
+    n, t = _gpu("greedy", d, logits)
+    rn, rt = oracle.verify_greedy(d, logits)
+    assert np.array_equal(n, rn) and np.array_equal(t, rt)
+    assert n[0] == (gamma if first_miss is None else first_miss)
+    # rejection: u = 0 accepts every drafted token with p(d) > 0 ... unless forced
+    p = np.exp(logits - logits.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    q = np.roll(p[:, :gamma], 1, axis=-1).astype(np.float32)
+    u = np.zeros((B, gamma + 1), np.float32)
+    u[:, gamma] = 0.37
+    if first_miss is not None:
+        p[:, first_miss, d[:, first_miss]] = 0.0   # p(d) = 0 < u q(d) for u > 0
+        u[:, first_miss] = 0.5
+    log(f"verify case long window reject first_miss={first_miss}")
+    n, t = _gpu("reject", d, p, q, u)
+    rn, rt = oracle.verify_reject(d, p, q, u)
+    assert np.array_equal(n, rn) and np.array_equal(t, rt)

@@ -81,3 +81,17 @@ def test_llava72b_shape_sampled_rows_and_top_k_selection():
 def test_deterministic():
     vs, xs = W.uv_hidden(W.C2, 1)
     assert np.array_equal(_gpu(vs, xs), _gpu(vs, xs))
+
+
+@pytest.mark.parametrize("n_vis,n_text,d", [(1, 1, 8), (37, 3, 72), (300, 5, 1000), (100, 4, 16384)])
+def test_edge_sizes(n_vis, n_text, d):
+    """One video and one text token at the smallest hidden size; hidden sizes
+    that are not multiples of 64 (the text sums work in 64-dim slices); the
+    largest hidden size, whose two text vectors take 128 KB of LDS."""
+    rng = np.random.default_rng(n_vis * 31 + d)
+    vs = [W.bf16_round(rng.standard_normal((n_vis, d)).astype(np.float32)) for _ in range(2)]
+    xs = [W.bf16_round(rng.standard_normal((n_text, d)).astype(np.float32)) for _ in range(2)]
+    log(f"uvprune case edge n_vis={n_vis} n_text={n_text} d={d}")
+    got = _gpu(vs, xs)
+    ref = oracle.uvprune_scores(vs, xs)
+    assert float(np.abs(got - ref).max()) <= 8e-6 * n_text

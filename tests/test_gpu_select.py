@@ -66,6 +66,16 @@ def test_long_rows_budget_edges(budget):
     _check(rows, F, H, Wd, 0.5, budget, f"long budget={budget}")
 
 
+@pytest.mark.parametrize("F,H,Wd", [(1, 1, 1), (1, 1, 2), (3, 1, 1), (1, 2, 2)])
+def test_tiny_rows_every_budget(F, H, Wd):
+    """Rows of one to four tokens, every budget from 0 to N, three Top-P values."""
+    N = F * H * Wd
+    rows = W.score_rows("lognormal2", 3, N, seed=14)
+    for top_p in (0.0, 0.5, 1.0):
+        for budget in range(N + 1):
+            _check(rows, F, H, Wd, top_p, budget, f"tiny N={N} P={top_p} B={budget}")
+
+
 def test_strided_rows():
     """Rows taken from a wider matrix (row stride > F*H*W), as from a slice."""
     from visual_kv_pruning_amd import ops

@@ -229,6 +229,7 @@ def main():
 
     # (2) per-kind launch durations: events around each graph replay, on the launch stream
     per_us = {}
+    spread = {}
     for kind in seqs:
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -238,6 +239,16 @@ def main():
         b.record()
         torch.cuda.synchronize()
         per_us[kind] = a.elapsed_time(b) * 1e3 / (args.steps * calls[kind])
+        # the spread over replays: an event pair around each one
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            graphs[kind].replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        reps = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / calls[kind] for i in range(args.steps)])
+        spread[kind] = {q: round(float(np.percentile(reps, p)), 3) for q, p in (("us_p10", 10), ("us_p50", 50),
+                                                                             ("us_p90", 90))}
 
     # (2b) parallel decoding on one GPU (ParallelVLM notes, "parallel decoding":
     # the draft produces the next window while the target verifies the last):
@@ -308,7 +319,7 @@ def main():
     score_flop = 2 * D * Hq * (T * NV + T * (T + 1) // 2) + 2 * D * Hq * T * NV
 
     kernels = {
-        k: {"us_avg": round(per_us[k], 3), "calls_per_step": calls[k]} for k in seqs
+        k: {"us_avg": round(per_us[k], 3), **spread[k], "calls_per_step": calls[k]} for k in seqs
     }
     kernels["verify_attn"].update(bytes=verify_bytes, gbs=round(verify_gbs, 1))
     kernels["draft_attn"].update(bytes=draft_bytes, gbs=round(draft_gbs, 1))

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SVLM_ABI_VERSION 1
+#define SVLM_ABI_VERSION 2
 
 enum svlm_status {
   SVLM_OK = 0,
@@ -137,10 +137,16 @@ int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh,
  * kept:     [R][budget] int32, ascending token indices (output).
  * n_stage1: [R] int32 k1 (output).  tag: [R][n_vis] uint8 or NULL
  *           (0 dropped, 1 stage I, 2 stage II).
- * ws:       svlm_select_workspace(R, n_vis) bytes.
+ * ws:       svlm_select_workspace(R, n_vis, budget, top_p) bytes, 16-byte
+ *           aligned (caller-owned, device memory).  It is 0 except for pure
+ *           top-K (top_p >= 1) on rows longer than 32768 tokens, which are
+ *           split into segments whose top-K candidates a second pass
+ *           reduces; the result is identical.  With tag != NULL that form is
+ *           not used and ws is ignored.  A workspace that is needed but
+ *           missing or short is SVLM_E_WORKSPACE.
  * Requires 0 <= budget <= n_vis <= 2^18.
  * ------------------------------------------------------------------------ */
-size_t svlm_select_workspace(int R, int n_vis);
+size_t svlm_select_workspace(int R, int n_vis, int budget, double top_p);
 int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, int W,
                 double top_p, int budget, int32_t* kept, int32_t* n_stage1, uint8_t* tag,
                 void* ws, size_t ws_bytes, void* stream);

@@ -31,14 +31,19 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svlm_abi_version() == 1
+    assert lib.svlm_abi_version() == L.ABI_VERSION == 2
     for st in range(5):
         assert lib.svlm_status_string(st)
     assert b"unknown" in lib.svlm_status_string(99)
 
 
 def test_workspace_queries_are_host_only(lib):
-    assert lib.svlm_select_workspace(4, 1000) == 0
+    assert lib.svlm_select_workspace(4, 1000, 100, 1.0) == 0
+    # the split top-K form needs a workspace: pure top-K on rows past 32768 tokens
+    assert lib.svlm_select_workspace(112, 141120, 1024, 1.0) > 0
+    assert lib.svlm_select_workspace(112, 141120, 1024, 0.5) == 0
+    assert lib.svlm_select_workspace(1, 32768, 1024, 1.0) == 0
+    assert lib.svlm_select_workspace(0, 141120, 1024, 1.0) == 0
     assert lib.svlm_verify_workspace(1, 5, 152064) > 0
     assert lib.svlm_verify_workspace(0, 5, 10) == 0
 
@@ -127,6 +132,13 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     assert lib.svlm_select(fake, 1 << 20, 1, 1024, 16, 17, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_UNSUPPORTED
     assert lib.svlm_select(fake, 20, 1, 2, 2, 5, float("nan"), 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID
     assert lib.svlm_select(fake, 10, 1, 2, 2, 5, 0.5, 2, fake, fake, NULL, NULL, 0, NULL) == L.SVLM_E_INVALID  # stride
+    # select: the split top-K form (pure top-K, rows past 32768 tokens, no tags)
+    # needs its workspace; with tags it takes the one-workgroup form and none
+    need = lib.svlm_select_workspace(2, 141120, 1024, 1.0)
+    assert lib.svlm_select(fake, 141120, 2, 720, 14, 14, 1.0, 1024, fake, fake, NULL, NULL, 0, NULL) \
+        == L.SVLM_E_WORKSPACE
+    assert lib.svlm_select(fake, 141120, 2, 720, 14, 14, 1.0, 1024, fake, fake, NULL, fake, need - 1, NULL) \
+        == L.SVLM_E_WORKSPACE
     # select with no rows is a no-op (nothing is launched, pointers may be null)
     assert lib.svlm_select(NULL, 20, 0, 2, 2, 5, 0.5, 2, NULL, NULL, NULL, NULL, 0, NULL) == L.SVLM_OK
     # gather: tail past the source, unsupported D

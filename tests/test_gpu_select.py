@@ -66,6 +66,64 @@ def test_long_rows_budget_edges(budget):
     _check(rows, F, H, Wd, 0.5, budget, f"long budget={budget}")
 
 
+def _check_split(rows, F, H, Wd, top_p, budget, name, pad=0):
+    """Pure top-K without tags: rows past 32768 tokens take the split form
+    (segment top-K, then a top-K over the candidates).  Kept lists and stage-I
+    counts must equal the oracle's, and the tagged one-workgroup form's."""
+    from visual_kv_pruning_amd import ops
+    R, N = rows.shape
+    log(f"select split case {name}: R={R} N={N} P={top_p} B={budget} pad={pad} "
+        f"ws={ops.select_workspace_bytes(R, N, budget, top_p)}")
+    wide = np.ones((R, N + pad), np.float32)   # padding past each row is never read
+    wide[:, :N] = rows
+    s = torch.from_numpy(wide).to("cuda:0")[:, :N]
+    kept, n1, _ = ops.select(s, F, H, Wd, top_p, budget)
+    kept_t, n1_t, _ = ops.select(s, F, H, Wd, top_p, budget, with_tag=True)
+    torch.cuda.synchronize()
+    rk, r1, _ = oracle.select_rows(rows, F, H, Wd, top_p, budget)
+    assert np.array_equal(n1.cpu().numpy(), r1), name
+    assert np.array_equal(kept.cpu().numpy(), rk.astype(np.int32)), name
+    assert np.array_equal(kept_t.cpu().numpy(), rk.astype(np.int32)), name
+    assert np.array_equal(n1_t.cpu().numpy(), r1), name
+
+
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+def test_split_topk_long_rows(kind):
+    """50 frames of 28 x 28 = 39200 tokens: two segments of 19600; budget 10%."""
+    F, H, Wd = 50, 28, 28
+    rows = W.score_rows(kind, 3, F * H * Wd, seed=21)
+    _check_split(rows, F, H, Wd, 1.0, 3920, f"split {kind}")
+
+
+@pytest.mark.parametrize("budget", [1, 2, 1024, 16383, 16384, 16385, 19600, 39199, 39200])
+def test_split_topk_budget_edges(budget):
+    """Budgets around the split form's limits (two segments of 19600 tokens):
+    2 x 16384 candidates fill one register-resident row (16385 does not, and
+    falls back to the one-workgroup form), the segment length, and the whole
+    row."""
+    F, H, Wd = 50, 28, 28
+    rows = W.score_rows("lognormal2", 2, F * H * Wd, seed=22)
+    _check_split(rows, F, H, Wd, 1.0, budget, f"split budget={budget}")
+
+
+def test_split_topk_ties_across_segments():
+    """Scores quantised to 1/64: long runs of equal scores cross every
+    segment boundary, so the index tie-break decides which tokens are kept."""
+    F, H, Wd = 50, 28, 28
+    rows = W.score_rows("lognormal2", 2, F * H * Wd, seed=23)
+    rows = (np.floor(rows / rows.max(axis=1, keepdims=True) * 64) / 64).astype(np.float32)
+    for budget in (1, 500, 3920, 9000):
+        _check_split(rows, F, H, Wd, 2.0, budget, f"split ties budget={budget}")
+
+
+def test_split_topk_hour_shape():
+    """The hour-long shape: 720 frames x 14 x 14 = 141120 tokens, top-K 1024
+    (6 segments of 23520), four rows, a strided view."""
+    F, H, Wd = 720, 14, 14
+    rows = W.score_rows("pareto1.1", 4, F * H * Wd, seed=24)
+    _check_split(rows, F, H, Wd, 1.0, 1024, "split hour", pad=40)
+
+
 @pytest.mark.parametrize("F,H,Wd", [(1, 1, 1), (1, 1, 2), (3, 1, 1), (1, 2, 2)])
 def test_tiny_rows_every_budget(F, H, Wd):
     """Rows of one to four tokens, every budget from 0 to N, three Top-P values."""

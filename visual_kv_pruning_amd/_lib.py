@@ -26,7 +26,7 @@ SIGNATURES = {
     "svlm_score_workspace": (sz, [i32, i32, i32, i32, i32]),
     "svlm_score": (i32, [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                          f32, i32, f32, f32, vp, vp, sz, vp]),
-    "svlm_select_workspace": (sz, [i32, i32]),
+    "svlm_select_workspace": (sz, [i32, i32, i32, f64]),
     "svlm_select": (i32, [vp, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, sz, vp]),
     "svlm_gather_kv": (i32, [vp, vp, i64, i64, i32, vp, i64, i32, i32, i32, vp, vp, i64, i64, i32, i32, i32, vp]),
     "svlm_decode_attn_workspace": (sz, [i32, i32, i32, i32, i32, i32, i32]),
@@ -40,6 +40,8 @@ SIGNATURES = {
     "svlm_verify_workspace": (sz, [i32, i32, i32]),
     "svlm_verify": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
 }
+
+ABI_VERSION = 2  # SVLM_ABI_VERSION of include/svlm.h
 
 _lib = None
 
@@ -60,6 +62,10 @@ def load() -> C.CDLL:
             f"libsvlm.so not found at {LIB_PATH}: build it with `python -m visual_kv_pruning_amd.build` "
             "(there is no non-HIP fallback)")
     lib = C.CDLL(LIB_PATH)
+    lib.svlm_abi_version.restype = C.c_int
+    if lib.svlm_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.svlm_abi_version()}, these bindings expect "
+                          f"{ABI_VERSION}: rebuild it")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -16,8 +16,14 @@
 // (above-threshold, tie) counts gives every token its stage-I rank, and the
 // stage-II picks before any remainder rank have a closed form, so `kept` is
 // written ascending without further scans.
+//
+// Pure top-K on long rows (the hour-long case: 112 rows of 141120 scores) is
+// split: one workgroup per row segment finds the segment's top K, and a
+// second pass takes the top K of the candidates, so the chip is not left with
+// one workgroup per row.
 #pragma clang fp contract(off)
 
+#include <algorithm>
 #include <cmath>
 
 #include "svlm_internal.h"
@@ -39,9 +45,20 @@ struct SelArgs {
   int N, budget;
   double top_p;
   int32_t* kept;
-  int32_t* n_stage1;
+  int64_t kept_stride;
+  int32_t* n_stage1;  // may be NULL (segment pass)
   uint8_t* tag;
+  // split top-K.  Segment pass: workgroup w takes segment p = w % segs of row
+  // r = w / segs (seg_len tokens, the last one shorter) with budget
+  // min(budget, its length) and writes its kept tokens and their scores to
+  // candidate slots r * C + p * budget + j.  Candidate pass: row r is the C
+  // candidate scores, and a kept position n is written as cand_tok[r * C + n].
+  int segs, seg_len, C;
+  float* cand_score;
+  int32_t* cand_tok;
 };
+
+enum : int { kPlain = 0, kSegmentPass = 1, kCandidatePass = 2 };
 
 __device__ __forceinline__ unsigned key_of(float s) {
   unsigned k = f_bits(s);
@@ -90,15 +107,26 @@ __device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm, uint64_t* total)
 // of the one-chunk case.
 // MASS: the row has a Top-P stage I (0 < top_p < 1), so per-token masses are
 // summed; pure top-K and fill-only selections count tokens alone.
-template <bool CHUNKED, bool MASS>
+template <bool CHUNKED, bool MASS, int SPLIT = kPlain>
 __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   constexpr int KREG = CHUNKED ? kChunkRunKeys : kRegKeys;
   // kCopies histogram copies, lane l adding to copy l % kCopies, so that at
   // most 64 / kCopies lanes of a wave meet on one counter (scores cluster in
   // a few exponents, and a shared counter serialises every lane on it); the
   // padded strides put one bin's copies in different banks
-  __shared__ unsigned h_cnt[kCopies * kCntStride];
-  __shared__ unsigned long long h_mass[kCopies * kMassStride];
+  // Rows held in registers share one LDS area between phases: the scores are
+  // staged through it with coalesced loads (thread t loads tokens t, t + 1024,
+  // ...; word i sits at i + i / 32, so the runs read back without bank
+  // conflicts), then it holds the level histograms, then the kept positions
+  // on their way to coalesced stores.  Chunked rows keep separate arrays.
+  constexpr int kCntWords = kCopies * kCntStride;
+  constexpr int kHistBytes = kCntWords * 4 + (MASS ? kCopies * kMassStride * 8 : 0);
+  constexpr int kStageWords = kThreads * kRegKeys + (kThreads * kRegKeys) / 32;
+  constexpr int kAreaBytes = CHUNKED ? kHistBytes : (kStageWords * 4 > kHistBytes ? kStageWords * 4 : kHistBytes);
+  __shared__ __align__(16) unsigned char area[kAreaBytes];
+  unsigned* const h_cnt = (unsigned*)area;
+  unsigned long long* const h_mass = (unsigned long long*)(area + kCntWords * 4);
+  unsigned* const stage = (unsigned*)area;
   __shared__ unsigned t_cnt[256];
   __shared__ unsigned long long t_mass[256];
   __shared__ unsigned long long sm_q[kWaves];
@@ -110,7 +138,17 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* srow = a.scores + (int64_t)row * a.row_stride;
-  const int N = a.N, B = a.budget;
+  int N = a.N, B = a.budget;
+  int64_t cand0 = 0;  // segment pass: this segment's first candidate slot
+  int tok0 = 0;       // and its first token
+  if constexpr (SPLIT == kSegmentPass) {
+    const int r = row / a.segs, p = row - r * a.segs;
+    tok0 = p * a.seg_len;
+    srow = a.scores + (int64_t)r * a.row_stride + tok0;
+    N = min(a.seg_len, a.N - tok0);
+    B = min(B, N);
+    cand0 = (int64_t)r * a.C + (int64_t)p * a.budget;
+  }
   constexpr int kChunk = kThreads * KREG;
   const int n_chunks = CHUNKED ? (N + kChunk - 1) / kChunk : 1;
   // this thread's run of tokens (in the current chunk): [n_begin, n_begin + n_mine)
@@ -124,8 +162,25 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
       n_begin = min(N, ch * kChunk + tid * KREG);
       n_mine = max(0, min(KREG, N - n_begin));
     }
+    if constexpr (CHUNKED) {
 #pragma unroll
-    for (int e = 0; e < KREG; ++e) keys[e] = key_of(srow[min(n_begin + e, N - 1)]);  // loads first, unconditional
+      for (int e = 0; e < KREG; ++e) keys[e] = key_of(srow[min(n_begin + e, N - 1)]);  // loads first, unconditional
+    } else {
+#pragma unroll
+      for (int e = 0; e < KREG; ++e) keys[e] = key_of(srow[min(e * kThreads + tid, N - 1)]);
+#pragma unroll
+      for (int e = 0; e < KREG; ++e) {
+        const int i = e * kThreads + tid;
+        if (i < N) stage[i + (i >> 5)] = keys[e];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < KREG; ++e) {
+        const int i = min(n_begin + e, N - 1);
+        keys[e] = stage[i + (i >> 5)];
+      }
+      __syncthreads();  // the area becomes the histograms
+    }
 #pragma unroll
     for (int e = 0; e < KREG; ++e) keys[e] = (e < n_mine) ? keys[e] : 0u;
   };
@@ -163,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
     unsigned prefix = 0;
     for (int i = tid; i < kCopies * kCntStride; i += kThreads) {
       h_cnt[i] = 0u;
-      h_mass[i] = 0ull;
+      if constexpr (MASS) h_mass[i] = 0ull;
     }
     __syncthreads();
     unsigned* const my_cnt = h_cnt + (lane % kCopies) * kCntStride;
@@ -186,19 +241,32 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
           if (e < n_mine) bin_key(keys[e]);
       }
       __syncthreads();
-      // one thread per bin adds up the copies and clears them for the next level
-      if (tid < 256) {
+      // four threads per bin add up a quarter of its copies each (clearing
+      // them for the next level), then combine across the four lanes
+      {
+        static_assert(kThreads == 4 * 256 && kCopies % 4 == 0, "four threads per bin");
+        const int bin = tid >> 2, c0 = (tid & 3) * (kCopies / 4);
         unsigned cc = 0;
         uint64_t mm = 0;
 #pragma unroll
-        for (int c = 0; c < kCopies; ++c) {
-          cc += h_cnt[c * kCntStride + tid];
-          mm += h_mass[c * kMassStride + tid];
-          h_cnt[c * kCntStride + tid] = 0u;
-          h_mass[c * kMassStride + tid] = 0ull;
+        for (int c = c0; c < c0 + kCopies / 4; ++c) {
+          cc += h_cnt[c * kCntStride + bin];
+          h_cnt[c * kCntStride + bin] = 0u;
+          if constexpr (MASS) {
+            mm += h_mass[c * kMassStride + bin];
+            h_mass[c * kMassStride + bin] = 0ull;
+          }
         }
-        t_cnt[tid] = cc;
-        t_mass[tid] = mm;
+        cc += __shfl_xor(cc, 1);
+        cc += __shfl_xor(cc, 2);
+        if constexpr (MASS) {
+          mm += __shfl_xor(mm, 1);
+          mm += __shfl_xor(mm, 2);
+        }
+        if ((tid & 3) == 0) {
+          t_cnt[bin] = cc;
+          t_mass[bin] = mm;
+        }
       }
       __syncthreads();
       // wave 0: the highest digit d whose bins d..255 (added to the keys
@@ -277,7 +345,11 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   const int m_fill = B - k1;
   const unsigned two_m = 2u * (unsigned)max(m_fill, 1);
   const unsigned step_q = (unsigned)(2 * n_rem) / two_m, step_r = (unsigned)(2 * n_rem) % two_m;
-  int32_t* const kept_row = a.kept + (int64_t)row * B;
+  int32_t* const kept_row = a.kept + (int64_t)row * a.kept_stride;
+  // register rows park each kept token's position (and, in the segment pass,
+  // its key) in LDS for the coalesced stores at the end
+  int* const kpos = (int*)area;
+  unsigned* const kkey = (unsigned*)area + B;
   uint8_t* const tag_row = a.tag ? a.tag + (int64_t)row * N : nullptr;
   unsigned carry_above = 0, carry_ties = 0;
   for (int ch = 0; ch < n_chunks; ++ch) {
@@ -323,6 +395,14 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
         next_r = (unsigned)(t % two_m);
       }
     }
+    auto put = [&](unsigned pos, int n, unsigned key) {
+      if constexpr (CHUNKED) {
+        kept_row[pos] = n;
+      } else {
+        kpos[pos] = n;
+        if constexpr (SPLIT == kSegmentPass) kkey[pos] = key;
+      }
+    };
     auto emit = [&](int e, unsigned key) {
       const int n = n_begin + e;
       const bool is_above = (k1 > 0) && key > vstar;
@@ -331,11 +411,11 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
       uint8_t tg = 0;
       if (s1) {
         tg = 1;
-        kept_row[s1_before + pb] = n;
+        put(s1_before + pb, n, key);
       } else {
         if ((unsigned)rho == next_q) {
           tg = 2;
-          kept_row[s1_before + pb] = n;
+          put(s1_before + pb, n, key);
           ++pb;
           if (pb < m_fill) {
             next_q += step_q;
@@ -360,7 +440,20 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
     for (int e = 0; e < KREG; ++e)
       if (e < n_mine) emit(e, keys[e]);
   }
-  if (tid == 0) a.n_stage1[row] = k1;
+  if constexpr (!CHUNKED) {
+    __syncthreads();
+    for (int j = tid; j < B; j += kThreads) {
+      if constexpr (SPLIT == kSegmentPass) {
+        a.cand_tok[cand0 + j] = tok0 + kpos[j];
+        a.cand_score[cand0 + j] = bits_f(kkey[j]);
+      } else if constexpr (SPLIT == kCandidatePass) {
+        kept_row[j] = a.cand_tok[(int64_t)row * a.C + kpos[j]];
+      } else {
+        kept_row[j] = kpos[j];
+      }
+    }
+  }
+  if (tid == 0 && a.n_stage1) a.n_stage1[row] = k1;
 }
 
 }  // namespace
@@ -368,17 +461,52 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
 
 using namespace svlm;
 
-extern "C" size_t svlm_select_workspace(int R, int n_vis) {
-  (void)R;
-  (void)n_vis;
-  return 0;  // everything lives in registers and LDS
+namespace {
+
+// Split top-K for long rows (pure top-K, no tags): every row is cut into
+// `segs` segments of seg_len tokens, each segment's top-K is found by its own
+// workgroup, and a second pass takes the top-K of the segments' candidates.
+// Exact: a token among the row's top K (score descending, index ascending)
+// has fewer than K tokens ahead of it in its segment, so it is among its
+// segment's top K; the candidate row keeps ascending token order, so the
+// second pass breaks ties exactly as a one-pass selection would.
+constexpr int kSegTargetKeys = 24576;  // tokens per segment workgroup (24 per thread)
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct SegPlan {
+  int segs = 1, seg_len = 0, C = 0;  // C: candidates per row
+};
+
+SegPlan seg_plan(int64_t N, int budget, double top_p) {
+  SegPlan sp;
+  constexpr int64_t cap = (int64_t)kThreads * kRegKeys;  // tokens of a register-resident row
+  if (!(top_p >= 1.0) || budget < 1 || N <= cap) return sp;
+  int64_t segs = (N + kSegTargetKeys - 1) / kSegTargetKeys;
+  int64_t seg = (N + segs - 1) / segs;
+  segs = (N + seg - 1) / seg;  // no empty last segment
+  if (seg < budget || segs * budget > cap) return sp;
+  sp.segs = (int)segs;
+  sp.seg_len = (int)seg;
+  sp.C = (int)((segs - 1) * budget + std::min<int64_t>(budget, N - (segs - 1) * seg));
+  return sp;
+}
+
+size_t seg_ws_bytes(int R, const SegPlan& sp, int budget) {
+  if (sp.segs <= 1) return 0;
+  return 2 * align256((size_t)R * sp.C * 4);  // candidate scores and tokens
+}
+
+}  // namespace
+
+extern "C" size_t svlm_select_workspace(int R, int n_vis, int budget, double top_p) {
+  if (R <= 0 || n_vis <= 0 || budget <= 0) return 0;
+  return seg_ws_bytes(R, seg_plan(n_vis, budget, top_p), budget);
 }
 
 extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, int W, double top_p,
                            int budget, int32_t* kept, int32_t* n_stage1, uint8_t* tag, void* ws, size_t ws_bytes,
                            void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (R < 0 || F < 1 || H < 1 || W < 1) return fail(SVLM_E_INVALID, "svlm_select: R >= 0 and F, H, W >= 1 required");
   const int64_t N = (int64_t)F * H * W;
   if (N > (1 << 18)) return fail(SVLM_E_UNSUPPORTED, "svlm_select: n_vis = F*H*W must be <= 2^18 (got %lld)", (long long)N);
@@ -394,11 +522,38 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   a.budget = budget;
   a.top_p = top_p;
   a.kept = kept;
+  a.kept_stride = budget;
   a.n_stage1 = n_stage1;
   a.tag = tag;
+  a.segs = 1;
+  a.seg_len = 0;
+  a.C = 0;
+  a.cand_score = nullptr;
+  a.cand_tok = nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  const SegPlan sp = seg_plan(N, budget, top_p);
+  if (sp.segs > 1 && !tag) {
+    const size_t need = seg_ws_bytes(R, sp, budget);
+    if (!ws || ws_bytes < need)
+      return fail(SVLM_E_WORKSPACE, "svlm_select: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_select: workspace must be 16-byte aligned");
+    a.cand_score = (float*)ws;
+    a.cand_tok = (int32_t*)((char*)ws + align256((size_t)R * sp.C * 4));
+    a.segs = sp.segs;
+    a.seg_len = sp.seg_len;
+    a.C = sp.C;
+    SelArgs s1 = a;
+    s1.n_stage1 = nullptr;
+    select_rows<false, false, kSegmentPass><<<R * sp.segs, kThreads, 0, st>>>(s1);
+    SelArgs s2 = a;
+    s2.scores = a.cand_score;
+    s2.row_stride = sp.C;
+    s2.N = sp.C;
+    select_rows<false, false, kCandidatePass><<<R, kThreads, 0, st>>>(s2);
+    return check_launch("svlm_select");
+  }
   const bool mass = top_p > 0.0 && top_p < 1.0;
   const bool chunked = N > (int64_t)kThreads * kRegKeys;
-  hipStream_t st = (hipStream_t)stream;
   if (chunked) {
     if (mass) select_rows<true, true><<<R, kThreads, 0, st>>>(a);
     else select_rows<true, false><<<R, kThreads, 0, st>>>(a);

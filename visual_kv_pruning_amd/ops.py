@@ -84,9 +84,14 @@ def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_st
 
 
 # ---------------------------------------------------------------------------
-def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: int, with_tag: bool = False):
+def select_workspace_bytes(R: int, n_vis: int, budget: int, top_p: float) -> int:
+    return int(L.load().svlm_select_workspace(R, n_vis, budget, float(top_p)))
+
+
+def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: int, with_tag: bool = False,
+           ws: torch.Tensor | None = None):
     """Two-stage selection per row.  scores [R][F*H*W] fp32 -> (kept [R][budget] int32, n_stage1 [R], tag)."""
-    _dev(scores)
+    _dev(scores, ws)
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be fp32 [R][n_vis] with contiguous rows")
     R, n = scores.shape
@@ -95,8 +100,12 @@ def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: i
     n1 = torch.empty(R, dtype=torch.int32, device=dev)
     tag = torch.empty(R, n, dtype=torch.uint8, device=dev) if with_tag else None
     row_stride = scores.stride(0) if R > 1 else n
+    need = 0 if with_tag else select_workspace_bytes(R, n, budget, top_p)
+    if need and ws is None:
+        ws = _ws(need, dev)
     L.call("svlm_select", scores.data_ptr(), row_stride, R, F, H, W, float(top_p), budget,
-           kept.data_ptr(), n1.data_ptr(), tag.data_ptr() if tag is not None else None, None, 0, _stream())
+           kept.data_ptr(), n1.data_ptr(), tag.data_ptr() if tag is not None else None,
+           ws.data_ptr() if need else None, _nbytes(ws) if need else 0, _stream())
     return kept, n1, tag
 
 

@@ -127,13 +127,16 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   unsigned* const h_cnt = (unsigned*)area;
   unsigned long long* const h_mass = (unsigned long long*)(area + kCntWords * 4);
   unsigned* const stage = (unsigned*)area;
-  __shared__ unsigned t_cnt[256];
-  __shared__ unsigned long long t_mass[256];
-  __shared__ unsigned long long sm_q[kWaves];
-  __shared__ uint64_t sm_scan[kWaves];
-  __shared__ unsigned sm_digit;
+  // level totals, double-buffered by level parity: every wave derives the
+  // level's digit from them, and the next level's totals go to the other
+  // buffer, so no barrier is needed after the digit search
+  __shared__ unsigned t_cnt[2][256];
+  __shared__ unsigned long long t_mass[2][256];
+  __shared__ unsigned sm_digit;  // Top-P rows: wave 0's digit and totals, broadcast
   __shared__ unsigned sm_cnt_above;
   __shared__ unsigned long long sm_mass_above;
+  __shared__ unsigned long long sm_q[kWaves];
+  __shared__ uint64_t sm_scan[kWaves];
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -264,67 +267,108 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
           mm += __shfl_xor(mm, 2);
         }
         if ((tid & 3) == 0) {
-          t_cnt[bin] = cc;
-          t_mass[bin] = mm;
+          t_cnt[level & 1][bin] = cc;
+          t_mass[level & 1][bin] = mm;
         }
       }
       __syncthreads();
-      // wave 0: the highest digit d whose bins d..255 (added to the keys
-      // above the prefix) reach the budget or the mass target
-      if (wv == 0) {
+      if constexpr (MASS) {
+        // Top-P rows: wave 0 finds the highest digit d whose bins d..255
+        // (added to the keys above the prefix) reach the budget or the mass
+        // target, and broadcasts it (one wave's 64-bit scans cost less than
+        // every wave's)
+        if (wv == 0) {
+          unsigned c4[4];
+          uint64_t m4[4];
+          unsigned ct = 0;
+          uint64_t mt = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // lane holds bins 255 - 4 lane - i (top-down)
+            const int bin = 255 - 4 * lane - i;
+            c4[i] = t_cnt[level & 1][bin];
+            m4[i] = t_mass[level & 1][bin];
+            ct += c4[i];
+            mt += m4[i];
+          }
+          uint64_t ci = ct, mi = mt;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint64_t yc = __shfl_up(ci, off);
+            const uint64_t ym = __shfl_up(mi, off);
+            if (lane >= off) {
+              ci += yc;
+              mi += ym;
+            }
+          }
+          uint64_t cb = ci - ct, mb = mi - mt;
+          int found = -1;
+          uint64_t c_above_d = 0, m_above_d = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint64_t c_incl = cb + c4[i], m_incl = mb + m4[i];
+            if (found < 0 && (cnt_above + c_incl >= (uint64_t)B || mass_above + m_incl >= Tm)) {
+              found = i;
+              c_above_d = cb;
+              m_above_d = mb;
+            }
+            cb = c_incl;
+            mb = m_incl;
+          }
+          // some bin always qualifies: all N >= B keys lie under the prefix at
+          // level 0, and the chosen bin qualifies again one level down
+          const unsigned long long hit = __builtin_amdgcn_ballot_w64(found >= 0);
+          const int first = (hit != 0ull) ? (int)__builtin_ctzll(hit) : 63;
+          if (lane == first) {
+            sm_digit = (unsigned)(255 - 4 * lane - (found >= 0 ? found : 3));
+            sm_cnt_above = cnt_above + (unsigned)c_above_d;
+            sm_mass_above = mass_above + m_above_d;
+          }
+        }
+        __syncthreads();
+        // read before the next level's wave-0 step rewrites them, which is two
+        // barriers away
+        prefix |= sm_digit << shift;
+        cnt_above = sm_cnt_above;
+        mass_above = sm_mass_above;
+      } else {
+        // count-only rows: every wave finds the digit from the totals itself
+        // (the next level's totals go to the other buffer, so no barrier
+        // follows)
+        const unsigned* const tc = t_cnt[level & 1];
         unsigned c4[4];
-        uint64_t m4[4];
         unsigned ct = 0;
-        uint64_t mt = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // lane holds bins 255 - 4 lane - i (top-down)
-          const int bin = 255 - 4 * lane - i;
-          c4[i] = t_cnt[bin];
-          m4[i] = t_mass[bin];
+          c4[i] = tc[255 - 4 * lane - i];
           ct += c4[i];
-          mt += m4[i];
         }
         // inclusive prefix over lanes, then the part above this lane's bins
-        uint64_t ci = ct, mi = mt;
+        // (counts stay below 2^19)
+        unsigned ci = ct;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const uint64_t yc = __shfl_up(ci, off);
-          const uint64_t ym = __shfl_up(mi, off);
-          if (lane >= off) {
-            ci += yc;
-            mi += ym;
-          }
+          const unsigned yc = __shfl_up(ci, off);
+          if (lane >= off) ci += yc;
         }
-        uint64_t cb = ci - ct, mb = mi - mt;
+        unsigned cb = ci - ct;
         int found = -1;
-        uint64_t c_above_d = 0, m_above_d = 0;
+        unsigned c_above_d = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint64_t c_incl = cb + c4[i], m_incl = mb + m4[i];
-          if (found < 0 && (cnt_above + c_incl >= (uint64_t)B || mass_above + m_incl >= Tm)) {
+          const unsigned c_incl = cb + c4[i];
+          if (found < 0 && cnt_above + c_incl >= (unsigned)B) {
             found = i;
             c_above_d = cb;
-            m_above_d = mb;
           }
           cb = c_incl;
-          mb = m_incl;
         }
-        // some bin always qualifies: all N >= B keys lie under the prefix at
-        // level 0, and the chosen bin qualifies again one level down
+        // some bin always qualifies (as above)
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(found >= 0);
         const int first = (hit != 0ull) ? (int)__builtin_ctzll(hit) : 63;
-        if (lane == first) {
-          sm_digit = (unsigned)(255 - 4 * lane - (found >= 0 ? found : 3));
-          sm_cnt_above = cnt_above + (unsigned)c_above_d;
-          sm_mass_above = mass_above + m_above_d;
-        }
+        const unsigned dig = (unsigned)(255 - 4 * lane - (found >= 0 ? found : 3));
+        prefix |= (unsigned)__builtin_amdgcn_readlane((int)dig, first) << shift;
+        cnt_above += (unsigned)__builtin_amdgcn_readlane((int)c_above_d, first);
       }
-      __syncthreads();
-      // read before the next level's wave-0 step rewrites them, which is two
-      // barriers away
-      prefix |= sm_digit << shift;
-      cnt_above = sm_cnt_above;
-      mass_above = sm_mass_above;
     }
     vstar = prefix;
     int c = B - (int)cnt_above;

@@ -116,6 +116,15 @@ def test_split_topk_ties_across_segments():
         _check_split(rows, F, H, Wd, 2.0, budget, f"split ties budget={budget}")
 
 
+def test_split_topk_long_segments():
+    """120 rows of 350 x 10 x 20 = 70000 tokens: three segments would take a
+    second round of workgroups on a 256-CU chip, so the plan keeps two
+    segments of 35000 tokens (36 per thread)."""
+    F, H, Wd = 350, 10, 20
+    rows = W.score_rows("lognormal3", 120, F * H * Wd, seed=25)
+    _check_split(rows, F, H, Wd, 1.0, 700, "split long segments")
+
+
 def test_split_topk_hour_shape():
     """The hour-long shape: 720 frames x 14 x 14 = 141120 tokens, top-K 1024
     (6 segments of 23520), four rows, a strided view."""

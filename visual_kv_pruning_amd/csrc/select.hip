@@ -34,6 +34,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRegKeys = 32;  // keys per thread held in registers (rows up to 32768 tokens)
+constexpr int kSegRegKeys = 36;   // keys per thread in the segment pass of the split top-K
 constexpr int kChunkRunKeys = 16;  // keys per thread per chunk for longer rows (fits 128 VGPRs)
 constexpr int kCopies = 32;
 constexpr int kCntStride = 257;   // words
@@ -109,7 +110,7 @@ __device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm, uint64_t* total)
 // summed; pure top-K and fill-only selections count tokens alone.
 template <bool CHUNKED, bool MASS, int SPLIT = kPlain>
 __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
-  constexpr int KREG = CHUNKED ? kChunkRunKeys : kRegKeys;
+  constexpr int KREG = CHUNKED ? kChunkRunKeys : (SPLIT == kSegmentPass ? kSegRegKeys : kRegKeys);
   // kCopies histogram copies, lane l adding to copy l % kCopies, so that at
   // most 64 / kCopies lanes of a wave meet on one counter (scores cluster in
   // a few exponents, and a shared counter serialises every lane on it); the
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   // on their way to coalesced stores.  Chunked rows keep separate arrays.
   constexpr int kCntWords = kCopies * kCntStride;
   constexpr int kHistBytes = kCntWords * 4 + (MASS ? kCopies * kMassStride * 8 : 0);
-  constexpr int kStageWords = kThreads * kRegKeys + (kThreads * kRegKeys) / 32;
+  constexpr int kStageWords = kThreads * KREG + (kThreads * KREG) / 32;
   constexpr int kAreaBytes = CHUNKED ? kHistBytes : (kStageWords * 4 > kHistBytes ? kStageWords * 4 : kHistBytes);
   __shared__ __align__(16) unsigned char area[kAreaBytes];
   unsigned* const h_cnt = (unsigned*)area;
@@ -514,7 +515,7 @@ namespace {
 // has fewer than K tokens ahead of it in its segment, so it is among its
 // segment's top K; the candidate row keeps ascending token order, so the
 // second pass breaks ties exactly as a one-pass selection would.
-constexpr int kSegTargetKeys = 24576;  // tokens per segment workgroup (24 per thread)
+constexpr int kSegTargetKeys = 24576;  // preferred tokens per segment workgroup (24 per thread)
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -522,14 +523,20 @@ struct SegPlan {
   int segs = 1, seg_len = 0, C = 0;  // C: candidates per row
 };
 
-SegPlan seg_plan(int64_t N, int budget, double top_p) {
+SegPlan seg_plan(int R, int64_t N, int budget, double top_p) {
   SegPlan sp;
-  constexpr int64_t cap = (int64_t)kThreads * kRegKeys;  // tokens of a register-resident row
-  if (!(top_p >= 1.0) || budget < 1 || N <= cap) return sp;
-  int64_t segs = (N + kSegTargetKeys - 1) / kSegTargetKeys;
+  constexpr int64_t cap = (int64_t)kThreads * kRegKeys;         // tokens of a register-resident row
+  constexpr int64_t seg_cap = (int64_t)kThreads * kSegRegKeys;  // tokens of one segment
+  if (!(top_p >= 1.0) || budget < 1 || N <= cap || R < 1) return sp;
+  // segments of about kSegTargetKeys tokens, but no more than the fewest
+  // possible take in the same number of rounds of one workgroup per CU
+  const int64_t fewest = (N + seg_cap - 1) / seg_cap, cus = num_cus();
+  auto rounds = [&](int64_t n) { return ((int64_t)R * n + cus - 1) / cus; };
+  int64_t segs = std::max(fewest, (N + kSegTargetKeys - 1) / kSegTargetKeys);
+  while (segs > fewest && rounds(segs) > rounds(fewest)) --segs;
   int64_t seg = (N + segs - 1) / segs;
   segs = (N + seg - 1) / seg;  // no empty last segment
-  if (seg < budget || segs * budget > cap) return sp;
+  if (segs < 2 || seg < budget || segs * budget > cap) return sp;
   sp.segs = (int)segs;
   sp.seg_len = (int)seg;
   sp.C = (int)((segs - 1) * budget + std::min<int64_t>(budget, N - (segs - 1) * seg));
@@ -545,7 +552,7 @@ size_t seg_ws_bytes(int R, const SegPlan& sp, int budget) {
 
 extern "C" size_t svlm_select_workspace(int R, int n_vis, int budget, double top_p) {
   if (R <= 0 || n_vis <= 0 || budget <= 0) return 0;
-  return seg_ws_bytes(R, seg_plan(n_vis, budget, top_p), budget);
+  return seg_ws_bytes(R, seg_plan(R, n_vis, budget, top_p), budget);
 }
 
 extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, int W, double top_p,
@@ -575,7 +582,7 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   a.cand_score = nullptr;
   a.cand_tok = nullptr;
   hipStream_t st = (hipStream_t)stream;
-  const SegPlan sp = seg_plan(N, budget, top_p);
+  const SegPlan sp = seg_plan(R, N, budget, top_p);
   if (sp.segs > 1 && !tag) {
     const size_t need = seg_ws_bytes(R, sp, budget);
     if (!ws || ws_bytes < need)

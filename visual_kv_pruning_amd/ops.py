@@ -90,7 +90,11 @@ def select_workspace_bytes(R: int, n_vis: int, budget: int, top_p: float) -> int
 
 def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: int, with_tag: bool = False,
            ws: torch.Tensor | None = None):
-    """Two-stage selection per row.  scores [R][F*H*W] fp32 -> (kept [R][budget] int32, n_stage1 [R], tag)."""
+    """Two-stage selection per row.  scores [R][F*H*W] fp32 -> (kept [R][budget] int32, n_stage1 [R], tag).
+
+    Pure top-K (top_p >= 1) on rows past 32768 tokens without tags runs split
+    over row segments and needs select_workspace_bytes(R, n_vis, budget, top_p)
+    bytes of device workspace: `ws` if given, else allocated here."""
     _dev(scores, ws)
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be fp32 [R][n_vis] with contiguous rows")

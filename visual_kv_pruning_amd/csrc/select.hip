@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
   const int m_fill = B - k1;
   const unsigned two_m = 2u * (unsigned)max(m_fill, 1);
   const unsigned step_q = (unsigned)(2 * n_rem) / two_m, step_r = (unsigned)(2 * n_rem) % two_m;
-  int32_t* const kept_row = a.kept + (int64_t)row * a.kept_stride;
+  int32_t* const kept_row = (SPLIT == kSegmentPass) ? nullptr : a.kept + (int64_t)row * a.kept_stride;
   // register rows park each kept token's position (and, in the segment pass,
   // its key) in LDS for the coalesced stores at the end
   int* const kpos = (int*)area;

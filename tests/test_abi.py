@@ -44,6 +44,30 @@ def test_workspace_queries_are_host_only(lib):
     assert lib.svlm_select_workspace(112, 141120, 1024, 0.5) == 0
     assert lib.svlm_select_workspace(1, 32768, 1024, 1.0) == 0
     assert lib.svlm_select_workspace(0, 141120, 1024, 1.0) == 0
+
+
+def test_split_select_plan(lib):
+    """The split top-K plan, seen through its workspace (2 x R x C x 4 bytes,
+    each half rounded up to 256; C = segments x budget).  Without a GPU the
+    chip is taken as 256 CUs."""
+    def ws(R, C):
+        half = (R * C * 4 + 255) // 256 * 256
+        return 2 * half
+    # 112 rows of 141120: 6 segments of ~24576 would need a third round of
+    # 1024-thread workgroups, so the fewest possible, 4 of 35280, are taken
+    assert lib.svlm_select_workspace(112, 141120, 1024, 1.0) == ws(112, 4 * 1024)
+    # 4 rows: 6 segments of 23520 fit one round
+    assert lib.svlm_select_workspace(4, 141120, 1024, 1.0) == ws(4, 6 * 1024)
+    # 2 segments of 19600 for 39200 tokens; 2 x 16384 candidates still fit
+    # one register-resident row, 2 x 16385 do not (one-workgroup form)
+    assert lib.svlm_select_workspace(3, 39200, 16384, 1.0) == ws(3, 2 * 16384)
+    assert lib.svlm_select_workspace(3, 39200, 16385, 2.0) == 0
+    # rows that fit one workgroup's registers are never split
+    assert lib.svlm_select_workspace(500, 32768, 10, 1.0) == 0
+    assert lib.svlm_select_workspace(100, 32769, 10, 1.0) == ws(100, 2 * 10)
+    # 500 such rows: two segments each would double the rounds of workgroups,
+    # and one segment is no split
+    assert lib.svlm_select_workspace(500, 32769, 10, 1.0) == 0
     assert lib.svlm_verify_workspace(1, 5, 152064) > 0
     assert lib.svlm_verify_workspace(0, 5, 10) == 0
 

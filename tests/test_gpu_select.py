@@ -183,3 +183,27 @@ def test_scores_from_the_value_model():
     p = W.prefill_layer(cfg, 0)
     row = oracle.aggregate_heads(oracle.score_layer(p.q_text, p.k, p.q_pos0, 0, cfg.n_vis, cfg.hkv), cfg.hkv, "all")
     _check(row.astype(np.float32), cfg.frames, cfg.gh, cfg.gw, cfg.top_p, cfg.budget, "tiny value model")
+
+
+def test_split_topk_workspace_errors():
+    """The split form names its workspace: a short one is an error, a
+    caller-supplied one of the queried size gives the oracle's result."""
+    from visual_kv_pruning_amd import ops
+    from visual_kv_pruning_amd._lib import SvlmError, SVLM_E_WORKSPACE
+    F, H, Wd = 50, 28, 28
+    N = F * H * Wd
+    rows = W.score_rows("lognormal1", 2, N, seed=26)
+    log("select split case workspace errors")
+    s = torch.from_numpy(rows).to("cuda:0")
+    need = ops.select_workspace_bytes(2, N, 500, 1.0)
+    assert need > 0
+    short = torch.empty(need - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(SvlmError) as e:
+        ops.select(s, F, H, Wd, 1.0, 500, ws=short)
+    assert e.value.status == SVLM_E_WORKSPACE
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    kept, n1, _ = ops.select(s, F, H, Wd, 1.0, 500, ws=ws)
+    torch.cuda.synchronize()
+    rk, r1, _ = oracle.select_rows(rows, F, H, Wd, 1.0, 500)
+    assert np.array_equal(kept.cpu().numpy(), rk.astype(np.int32))
+    assert np.array_equal(n1.cpu().numpy(), r1)

@@ -108,9 +108,11 @@ __device__ uint64_t block_excl_scan64(uint64_t x, uint64_t* sm, uint64_t* total)
 // of the one-chunk case.
 // MASS: the row has a Top-P stage I (0 < top_p < 1), so per-token masses are
 // summed; pure top-K and fill-only selections count tokens alone.
-template <bool CHUNKED, bool MASS, int SPLIT = kPlain>
+// KR: keys per thread of a register-resident row when not the default (a
+// candidate row of at most kThreads * KR tokens)
+template <bool CHUNKED, bool MASS, int SPLIT = kPlain, int KR = kRegKeys>
 __global__ __launch_bounds__(kThreads) void select_rows(SelArgs a) {
-  constexpr int KREG = CHUNKED ? kChunkRunKeys : (SPLIT == kSegmentPass ? kSegRegKeys : kRegKeys);
+  constexpr int KREG = CHUNKED ? kChunkRunKeys : (SPLIT == kSegmentPass ? kSegRegKeys : KR);
   // kCopies histogram copies, lane l adding to copy l % kCopies, so that at
   // most 64 / kCopies lanes of a wave meet on one counter (scores cluster in
   // a few exponents, and a shared counter serialises every lane on it); the
@@ -600,7 +602,8 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
     s2.scores = a.cand_score;
     s2.row_stride = sp.C;
     s2.N = sp.C;
-    select_rows<false, false, kCandidatePass><<<R, kThreads, 0, st>>>(s2);
+    if (sp.C <= kThreads * 8) select_rows<false, false, kCandidatePass, 8><<<R, kThreads, 0, st>>>(s2);
+    else select_rows<false, false, kCandidatePass><<<R, kThreads, 0, st>>>(s2);
     return check_launch("svlm_select");
   }
   const bool mass = top_p > 0.0 && top_p < 1.0;

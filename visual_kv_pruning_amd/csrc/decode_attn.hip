@@ -709,12 +709,13 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
   const int steps = (max_kv_len + kStep - 1) / kStep;
   int splits = num_splits;
   if (splits <= 0) {
-    // Workgroups for about three quarters of the compute units: the key loop
-    // is bound by HBM bandwidth well before every unit is busy, while each
-    // extra split adds partial state for the merge.  No split shorter than
+    // Workgroups for about seven eighths of the compute units: the key loop
+    // is bound by HBM bandwidth before every unit is busy, each extra split
+    // adds partial state for the merge, and one workgroup past the chip
+    // (one per CU) starts a second round.  No split shorter than
     // kMinStepsPerSplit steps.
     const int units = std::max(1, batch * Hkv * p.row_chunks);
-    splits = std::max(1, (3 * num_cus() / 4 + units - 1) / units);
+    splits = std::max(1, (7 * num_cus() / 8 + units - 1) / units);
     splits = std::min(splits, std::max(1, steps / kMinStepsPerSplit));
   }
   splits = std::max(1, std::min(splits, steps));

@@ -41,9 +41,14 @@
  *   - Device data that the host cannot see (indices, lengths, scores) are
  *     preconditions, stated per call; kernels clamp them so that no access
  *     leaves the buffers, but results are unspecified when they are violated.
- *   - Only D in {64, 128} and bf16 (SVLM_BF16) attention operands are
- *     supported; the innermost (D) dimension must be contiguous and every
- *     row 16-byte aligned.
+ *   - Only D in {64, 128} is supported; the innermost (D) dimension must be
+ *     contiguous and every row 16-byte aligned (strides in multiples of 16
+ *     bytes).
+ *   - Operand types: SVLM_BF16 runs the tuned matrix-core kernels.  SVLM_F32
+ *     (svlm_score, svlm_gather_kv, svlm_decode_attn[_indexed]) takes fp32
+ *     q, k and v as given, for the tiny fp32 reference configuration: plain
+ *     vector-ALU fp32 kernels with natural-base exp, correct at any size but
+ *     not tuned for bandwidth.  Outputs are fp32 either way.
  *   - Selection, gather and acceptance are bit-deterministic; score and
  *     attention are run-to-run deterministic (fixed reduction order).
  *   - Calls on different streams may run concurrently if their workspaces
@@ -59,12 +64,12 @@
 extern "C" {
 #endif
 
-#define SVLM_ABI_VERSION 2
+#define SVLM_ABI_VERSION 3
 
 enum svlm_status {
   SVLM_OK = 0,
   SVLM_E_INVALID = 1,     /* an argument is out of range, null or misaligned */
-  SVLM_E_UNSUPPORTED = 2, /* a valid request this build does not implement (dtype, D) */
+  SVLM_E_UNSUPPORTED = 2, /* a valid request this build does not implement (dtype, D, sizes) */
   SVLM_E_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace() size */
   SVLM_E_HIP = 4          /* the HIP runtime reported an error */
 };
@@ -95,19 +100,20 @@ const char* svlm_last_error(void);
  *     out = alpha * agg(A) + beta * out        (beta == 0: out is not read)
  * which lets several layers be averaged into one row set.
  *
- * q_text: [T][Hq][D] bf16 with strides q_st (per text token) and q_sh (per
- *         head); D contiguous.
- * k:      [Hkv][n_ctx][D] bf16 with strides k_sh, k_sn.
+ * q_text: [T][Hq][D] (dtype: SVLM_BF16 or SVLM_F32) with strides q_st (per
+ *         text token) and q_sh (per head); D contiguous.
+ * k:      [Hkv][n_ctx][D], same dtype, with strides k_sh, k_sn.
  * out:    fp32 rows, contiguous [rows][n_vis].
  * ws:     svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis) bytes (per-split row
- *         statistics and per-head score rows).
+ *         statistics and per-head score rows; with SVLM_F32 only the row
+ *         log-sum-exps, which fit in the same size).
  * Requires 1 <= T <= 128, scale > 0, q_pos0 + T <= n_ctx, 0 <= vis_start, vis_start + n_vis
  * <= q_pos0 + 1 (every visual key visible to every text query), n_vis <= 2^18,
  * and ((T-1)*q_st + D)*2 and (n_ctx + 1024)*k_sn*2 below 2^31 (32-bit buffer
- * ranges; SVLM_E_UNSUPPORTED otherwise).
+ * ranges; SVLM_E_UNSUPPORTED otherwise; the 32-bit limits apply to SVLM_BF16).
  * Computes QK^T on bf16 matrix cores with fp32 accumulation, in two passes
  * (row log-sum-exp, then normalised column sums); the score matrix is never
- * stored.
+ * stored.  SVLM_F32 runs the same two passes in fp32 vector arithmetic.
  * ------------------------------------------------------------------------ */
 size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis);
 int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh,
@@ -160,6 +166,7 @@ int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, in
  *   dst[g, n_idx + j] = src[g, tail_start + j],      j < n_tail
  * (the tail carries the always-kept text rows).  Applied to K and V alike.
  * src: [Hkv][n_src][D] with strides s_sh, s_sn; dst: strides d_sh, d_sn.
+ * dtype SVLM_BF16 or SVLM_F32 (2- or 4-byte elements; a bit-exact copy).
  * idx_sh = 0: one list for all heads; otherwise per-head lists.
  * Indices outside [0, n_src) are a precondition violation; such rows are
  * written as zeros.  Requires tail_start + n_tail <= n_src.  With
@@ -181,8 +188,9 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
  * n < L(b,i) with L = kv_len[b] - nq + i + 1 if causal_tail else kv_len[b]:
  *   out[b,i,h] = sum_n softmax_n(scale*<q[b,i,h], k[b,g,n]>) * v[b,g,n]
  *   lse[b,i,h] = log sum_n exp(scale*<q[b,i,h], k[b,g,n]>)   (natural log)
- * q:   [B][nq][Hq][D] bf16, batch stride q_sb, the rest contiguous.
- * k,v: [B][Hkv][max_kv_len][D] bf16 with strides kv_sb, kv_sh, kv_sn.
+ * q:   [B][nq][Hq][D] (dtype), batch stride q_sb, the rest contiguous.
+ * k,v: [B][Hkv][max_kv_len][D] (dtype) with strides kv_sb, kv_sh, kv_sn;
+ *      kv_sb = 0 shares one cache among the batch entries.
  * kv_len: [B] int32 on the device; precondition nq <= kv_len[b] <=
  *         max_kv_len (values are clamped into [0, max_kv_len]).
  * out: [B][nq][Hq][D] fp32 contiguous; lse: [B][nq][Hq] fp32 or NULL.
@@ -191,13 +199,15 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
  *   to ws and are merged in a fixed order.
  * ws: svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits)
  *   bytes (0 when one split suffices); no initial contents are needed.  Two
- *   calls that overlap in time must not share a workspace.
+ *   calls that overlap in time must not share a workspace.  SVLM_F32 uses no
+ *   workspace (ws may be NULL).
  * Requires scale > 0, nq*Hq*D*2 < 2^31, and one key split's rows times
  * kv_sn*2 below 2^31 bytes (always true when (max_kv_len + 576)*kv_sn*2 <
  * 2^31; SVLM_E_UNSUPPORTED otherwise).
- * Works in bf16 matrix-core products with fp32 accumulation; the softmax
- * weights enter the value product as a bf16 hi + lo pair, so the output
- * keeps fp32-level accuracy.
+ * SVLM_BF16 works in bf16 matrix-core products with fp32 accumulation; the
+ * softmax weights enter the value product as a bf16 hi + lo pair, so the
+ * output keeps fp32-level accuracy.  SVLM_F32: fp32 vector arithmetic, one
+ * wave per output row.
  * ------------------------------------------------------------------------ */
 size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len,
                                   int num_splits);
@@ -218,12 +228,15 @@ int svlm_decode_attn(const void* q, int64_t q_sb,
  *   r = kv_idx[b * idx_sb + g * idx_sh + n]
  * of k, v: [B][Hkv][kv_rows][D] bf16 with strides kv_sb, kv_sh, kv_sn.
  * idx_sh = 0: one list for all heads; idx_sb = 0: one list for all batch
- * entries.  The attention is svlm_decode_attn's with k[b,g,n] replaced by
- * row r, and kv_len by n_idx (device int32 [B], precondition
- * nq <= n_idx[b] <= max_n_idx; causal_tail applies to the last nq list
- * positions).  Indices are a precondition in [0, kv_rows); one outside
+ * entries.  List (b, g) has n_idx[b * n_sb + g * n_sh] entries (device
+ * int32): n_sh = 0 gives one length per batch entry, n_sh = 1 and
+ * n_sb = Hkv ragged per-head lengths (the per-layer, per-head selection of
+ * [StD-sel]).  The attention is svlm_decode_attn's with k[b,g,n] replaced
+ * by row r and kv_len by the list's length (precondition
+ * nq <= length <= max_n_idx; causal_tail applies to the last nq positions of
+ * each list).  Indices are a precondition in [0, kv_rows); one outside
  * reads a zero row (the result is then undefined) and never reads memory
- * outside the cache.  Requires kv_rows * kv_sn * 2 < 2^31.
+ * outside the cache.  Requires kv_rows * kv_sn * 2 < 2^31 (SVLM_BF16).
  * ws: svlm_decode_attn_indexed_workspace(...) bytes, same rules as above.
  * ------------------------------------------------------------------------ */
 size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_n_idx,
@@ -231,7 +244,7 @@ size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, int Hkv, in
 int svlm_decode_attn_indexed(const void* q, int64_t q_sb,
                              const void* k, const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
                              int kv_rows, const int32_t* kv_idx, int64_t idx_sb, int64_t idx_sh,
-                             const int32_t* n_idx, int max_n_idx,
+                             const int32_t* n_idx, int64_t n_sb, int64_t n_sh, int max_n_idx,
                              int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
                              int causal_tail, float* out, float* lse,
                              int num_splits, void* ws, size_t ws_bytes, void* stream);

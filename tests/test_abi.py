@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svlm_abi_version() == L.ABI_VERSION == 2
+    assert lib.svlm_abi_version() == L.ABI_VERSION == 3
     for st in range(5):
         assert lib.svlm_status_string(st)
     assert b"unknown" in lib.svlm_status_string(99)
@@ -87,7 +87,9 @@ def test_decode_attn_rejects_bad_arguments(lib):
     fake = C.c_void_p(4096)   # never dereferenced: validation fails first
     ok = dict(q=fake, k=fake, v=fake, kv_len=fake, out=fake)
     assert _attn(lib, D=96, **ok) == L.SVLM_E_UNSUPPORTED
-    assert _attn(lib, dtype=L.SVLM_F32, **ok) == L.SVLM_E_UNSUPPORTED
+    assert _attn(lib, dtype=7, **ok) == L.SVLM_E_UNSUPPORTED
+    # fp32 operands: rows of 16-byte multiples (4 elements), so 100 passes and 102 fails
+    assert _attn(lib, dtype=L.SVLM_F32, kv_sn=102, **ok) == L.SVLM_E_INVALID
     assert _attn(lib) == L.SVLM_E_INVALID                              # null pointers
     assert _attn(lib, Hq=6, Hkv=4, **ok) == L.SVLM_E_INVALID          # Hq % Hkv
     assert _attn(lib, nq=0, **ok) == L.SVLM_E_INVALID
@@ -105,7 +107,7 @@ def test_decode_attn_rejects_bad_arguments(lib):
 
 def _attn_idx(lib, **kw):
     args = dict(q=NULL, q_sb=0, k=NULL, v=NULL, kv_sb=0, kv_sh=0, kv_sn=128, kv_rows=100, kv_idx=NULL, idx_sb=0,
-                idx_sh=0, n_idx=NULL, max_n_idx=10, dtype=L.SVLM_BF16, batch=1, nq=1, Hq=8, Hkv=2, D=128,
+                idx_sh=0, n_idx=NULL, n_sb=1, n_sh=0, max_n_idx=10, dtype=L.SVLM_BF16, batch=1, nq=1, Hq=8, Hkv=2, D=128,
                 scale=0.1, causal=0, out=NULL, lse=NULL, num_splits=0, ws=NULL, ws_bytes=0, stream=NULL)
     args.update(kw)
     return lib.svlm_decode_attn_indexed(*args.values())
@@ -119,6 +121,8 @@ def test_decode_attn_indexed_rejects_bad_arguments(lib):
     assert _attn_idx(lib, kv_rows=0, **ok) == L.SVLM_E_INVALID
     assert _attn_idx(lib, kv_rows=1 << 24, **ok) == L.SVLM_E_INVALID   # 2^24 rows x 256 B > 2^31
     assert _attn_idx(lib, idx_sh=-1, **ok) == L.SVLM_E_INVALID
+    assert _attn_idx(lib, n_sh=-1, **ok) == L.SVLM_E_INVALID
+    assert b"length" in lib.svlm_last_error()
     assert _attn_idx(lib, D=96, **ok) == L.SVLM_E_UNSUPPORTED
     # a long list needs more splits than asked for: the split length is capped
     # (the split's list is staged on chip), so the workspace is never zero
@@ -168,6 +172,9 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     # gather: tail past the source, unsupported D
     assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 8, 3, fake, fake, 0, 128, 1, 128, 0, NULL) == L.SVLM_E_INVALID
     assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 0, 3, fake, fake, 0, 128, 1, 80, 0, NULL) == L.SVLM_E_UNSUPPORTED
+    assert lib.svlm_gather_kv(fake, fake, 0, 128, 10, fake, 0, 3, 0, 3, fake, fake, 0, 128, 1, 128, 5, NULL) == L.SVLM_E_UNSUPPORTED
+    # fp32 rows: a row stride of 68 elements is 272 bytes (a 16-byte multiple), 66 is not
+    assert lib.svlm_gather_kv(fake, fake, 0, 66, 10, fake, 0, 3, 0, 3, fake, fake, 0, 64, 1, 64, 1, NULL) == L.SVLM_E_INVALID
     # score: T too large, visual range beyond what text sees, non-positive scale
     args = [fake, 1024, 128, fake, 1 << 16, 128, 0, 200, 300, 100, 0, 50, 8, 2, 128, 0.1, 2, 1.0, 0.0, fake, fake, 1 << 20, NULL]
     assert lib.svlm_score(*args) == L.SVLM_E_UNSUPPORTED

@@ -1,5 +1,7 @@
-"""Mean text->visual attention on the GPU vs the fp64 oracle: within 1e-5 absolute
-(and the relative error on scores >= 1e-6 reported)."""
+"""Mean text->visual attention on the GPU vs the fp64 oracle: within 1e-5
+absolute (the contract).  Scores are ~1e-5 to 4e-5 at the full shapes, so the
+absolute bound alone is loose; a regression bound is asserted beside it:
+relative error <= 1e-4 on every score >= 1e-6 (the kernels reach ~3e-6)."""
 import dataclasses
 
 import numpy as np
@@ -12,6 +14,8 @@ from tests._util import dev_bf16, log
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 ABS_TOL = 1e-5
+REL_TOL = 1e-4       # regression bound on scores >= 1e-6
+F32_REL_TOL = 1e-5   # fp32 operands
 
 
 def _gpu_score(p, cfg, agg, n_vis=None, vis_start=0):
@@ -28,12 +32,13 @@ def _ref(p, cfg, agg, n_vis=None, vis_start=0):
     return oracle.aggregate_heads(sq, cfg.hkv, {"qhead": "qhead", "kvhead": "kvhead", "all": "all"}[agg])
 
 
-def _compare(got, ref, name):
+def _compare(got, ref, name, rel_tol=REL_TOL):
     err = float(np.abs(got - ref).max())
     big = ref >= 1e-6
     rel = float((np.abs(got - ref)[big] / ref[big]).max()) if big.any() else 0.0
     log(f"score {name}: max abs err {err:.2e}, max rel err (scores >= 1e-6) {rel:.2e}")
     assert err <= ABS_TOL, name
+    assert rel <= rel_tol, f"{name}: relative error {rel:.2e} above the regression bound"
     return rel
 
 
@@ -151,3 +156,65 @@ def test_edge_shapes(D, T, n_vis, pre, post, Hq, Hkv):
     for agg in ("qhead", "kvhead", "all"):
         _compare(_gpu_score(p, shape, agg, n_vis=n_vis, vis_start=pre), _ref(p, shape, agg, n_vis, pre),
                  f"edge {agg}")
+
+
+def test_hour_long_layer_sampled_kv_heads():
+    """The hour-long shape (141120 visual + 64 text tokens, 28 q / 4 KV heads)
+    at full size with one row per KV head, the signal its per-(layer, KV head)
+    top-K consumes; the oracle checks KV heads 0 and 3 (their 7 q heads each)."""
+    cfg = W.C5
+    p = W.prefill_layer(cfg, 0)
+    log("score case hour-long layer, per KV head")
+    got = _gpu_score(p, cfg, "kvhead")
+    G = cfg.group
+    for g in (0, cfg.hkv - 1):
+        heads = list(range(g * G, (g + 1) * G))
+        sq = oracle.score_layer(p.q_text[:, heads], p.k[g:g + 1], p.q_pos0, 0, cfg.n_vis, 1)
+        ref = oracle.aggregate_heads(sq, 1, "kvhead")
+        _compare(got[g:g + 1], ref, f"hour-long kv head {g}")
+
+
+def test_two_layers_per_layer_rows_match_oracle_rows():
+    """Several layers into the per-layer rows of the 32B-shape selection and the
+    per-(layer, KV head) rows of the hour-long selection, against the oracle's
+    multi-layer row builder (reduced context so the oracle stays quick)."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C1
+    layers = [W.prefill_layer(cfg, l) for l in range(3)]
+    log("score case multi-layer rows")
+    per_layer = torch.empty(3, cfg.n_vis, device="cuda:0")
+    per_kv = torch.empty(3 * cfg.hkv, cfg.n_vis, device="cuda:0")
+    one = torch.empty(1, cfg.n_vis, device="cuda:0")
+    for l, p in enumerate(layers):
+        ops.score(dev_bf16(p.q_text), dev_bf16(p.k), p.q_pos0, cfg.n_vis, agg="all", out=per_layer[l:l + 1])
+        ops.score(dev_bf16(p.q_text), dev_bf16(p.k), p.q_pos0, cfg.n_vis, agg="kvhead",
+                  out=per_kv[l * cfg.hkv:(l + 1) * cfg.hkv])
+        ops.score(dev_bf16(p.q_text), dev_bf16(p.k), p.q_pos0, cfg.n_vis, agg="all", alpha=1.0 / 3,
+                  beta=0.0 if l == 0 else 1.0, out=one)
+    torch.cuda.synchronize()
+    qk = [(p.q_text, p.k) for p in layers]
+    _compare(per_layer.cpu().numpy(), oracle.score_rows_for_config(qk, cfg.n_vis, cfg.n_vis, cfg.hkv, "layer"),
+             "rows per layer")
+    _compare(per_kv.cpu().numpy(),
+             oracle.score_rows_for_config(qk, cfg.n_vis, cfg.n_vis, cfg.hkv, "layer_kvhead"), "rows per kv head")
+    _compare(one.cpu().numpy(), oracle.score_rows_for_config(qk, cfg.n_vis, cfg.n_vis, cfg.hkv, "all"),
+             "one row over layers")
+
+
+@pytest.mark.parametrize("agg", ["qhead", "kvhead", "all"])
+def test_tiny_config_fp32_operands(agg):
+    """The tiny reference configuration in fp32: unrounded q and k through the
+    plain fp32 kernels against the oracle on the same values."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C1
+    p = W.prefill_layer(cfg, 0, round_bf16=False)
+    assert np.any(W.bf16_round(p.q_text) != p.q_text)
+    log(f"score case tiny fp32 agg={agg}")
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+    out = ops.score(f32(p.q_text), f32(p.k), p.q_pos0, cfg.n_vis, agg=agg)
+    out2 = ops.score(f32(p.q_text), f32(p.k), p.q_pos0, cfg.n_vis, agg=agg, alpha=0.5, beta=0.25,
+                     out=out.clone())
+    torch.cuda.synchronize()
+    ref = _ref(p, cfg, agg)
+    _compare(out.cpu().numpy(), ref, f"tiny fp32/{agg}", rel_tol=F32_REL_TOL)
+    _compare(out2.cpu().numpy(), 0.75 * ref, f"tiny fp32/{agg} alpha beta", rel_tol=F32_REL_TOL)

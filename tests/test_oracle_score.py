@@ -116,3 +116,67 @@ def test_sink_and_salient_tokens_stand_out():
     sc = oracle.aggregate_heads(oracle.score_layer(p.q_text, p.k, p.q_pos0, 0, cfg.n_vis, cfg.hkv), cfg.hkv, "all")[0]
     med = np.median(sc)
     assert np.all(sc[p.salient] > med)
+
+
+def test_aggregate_heads_hand_case():
+    """Hand-computed group and overall means of a 4-head, 3-token score table
+    (two KV heads of two q heads each)."""
+    sq = np.array([[1.0, 2.0, 3.0],
+                   [3.0, 6.0, 1.0],
+                   [0.0, 4.0, 8.0],
+                   [4.0, 0.0, 4.0]])
+    assert np.array_equal(oracle.aggregate_heads(sq, 2, "qhead"), sq)
+    assert np.array_equal(oracle.aggregate_heads(sq, 2, "kvhead"), [[2.0, 4.0, 2.0], [2.0, 2.0, 6.0]])
+    assert np.array_equal(oracle.aggregate_heads(sq, 2, "all"), [[2.0, 3.0, 4.0]])
+    assert np.array_equal(oracle.aggregate_heads(sq, 1, "kvhead"), [[2.0, 3.0, 4.0]])
+    assert np.array_equal(oracle.aggregate_heads(sq, 4, "kvhead"), sq)
+
+
+def _one_hot_layers(targets, T, D, hkv, n_vis, n_text):
+    """Layers whose q head h sends every text query's whole softmax to one
+    visual token targets[l][h]: that token's key is the unit vector e_h of its
+    KV head (all other keys are zero), and every query of head h is 400 e_h,
+    so its logit is 400/sqrt(D) = 100 above every other key's (exp(-100) is
+    far below fp64 resolution of 1)."""
+    layers = []
+    Hq = len(targets[0])
+    G = Hq // hkv
+    for tl in targets:
+        q = np.zeros((T, Hq, D), np.float32)
+        k = np.zeros((hkv, n_vis + n_text, D), np.float32)
+        for h, tok in enumerate(tl):
+            q[:, h, h] = 400.0
+            k[h // G, tok, h] = 1.0
+        layers.append((q, k))
+    return layers
+
+
+def test_score_rows_for_config_one_hot_closed_form():
+    """Each (layer, q head) puts all its attention on one known visual token,
+    so its score row is exactly an indicator.  The rows then follow by hand:
+    a (layer, KV head) row holds 1/G at its group's targets, a layer row 1/Hq
+    at the layer's targets, and the single row 1/(L Hq) at every target
+    (a token named twice collects twice)."""
+    T, D, hkv, n_vis, n_text = 3, 16, 2, 12, 3
+    targets = [[0, 5, 7, 11], [5, 2, 9, 9], [1, 1, 4, 6]]      # [layer][q head], G = 2
+    L, Hq, G = len(targets), len(targets[0]), 2
+    layers = _one_hot_layers(targets, T, D, hkv, n_vis, n_text)
+    kvh = oracle.score_rows_for_config(layers, n_vis, n_vis, hkv, "layer_kvhead")
+    lay = oracle.score_rows_for_config(layers, n_vis, n_vis, hkv, "layer")
+    one = oracle.score_rows_for_config(layers, n_vis, n_vis, hkv, "all")
+    want_kvh = np.zeros((L * hkv, n_vis))
+    want_lay = np.zeros((L, n_vis))
+    want_one = np.zeros((1, n_vis))
+    for l, tl in enumerate(targets):
+        for h, tok in enumerate(tl):
+            want_kvh[l * hkv + h // G, tok] += 1.0 / G
+            want_lay[l, tok] += 1.0 / Hq
+            want_one[0, tok] += 1.0 / (L * Hq)
+    assert kvh.shape == want_kvh.shape and np.allclose(kvh, want_kvh, atol=1e-15)
+    assert lay.shape == want_lay.shape and np.allclose(lay, want_lay, atol=1e-15)
+    assert one.shape == want_one.shape and np.allclose(one, want_one, atol=1e-15)
+    # spot values, written out: layer 1, KV head 1 holds token 9 twice
+    assert kvh[1 * hkv + 1, 9] == pytest.approx(1.0, abs=1e-15)
+    assert one[0, 5] == pytest.approx(2.0 / 12.0, abs=1e-15)
+    with pytest.raises(ValueError):
+        oracle.score_rows_for_config(layers, n_vis, n_vis, hkv, "rows")

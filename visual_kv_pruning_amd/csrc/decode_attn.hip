@@ -44,7 +44,8 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   int64_t kv_sb, kv_sh, kv_sn;
-  const int32_t* kv_len;
+  const int32_t* kv_len;  // key count of (b, h) at kv_len[b * len_sb + h * len_sh]
+  int64_t len_sb, len_sh;
   int max_kv_len;
   int batch, nq, Hq, Hkv, G, rows;
   float c;  // scale * log2(e)
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   const int b = ph / a.Hkv;
   const int row_base = blockIdx.y * RP;
 
-  const int n_kv = min(max(a.kv_len[b], 0), a.max_kv_len);
+  const int n_kv = min(max(a.kv_len[(int64_t)b * a.len_sb + (int64_t)h * a.len_sh], 0), a.max_kv_len);
   const int k_begin = s * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, n_kv);
   // this wave's blocks: keys k_begin + 64 j + 16 wave, j < n_my
@@ -752,11 +753,12 @@ constexpr int kIdxMaxSteps = kMaxIdxSplit / kStep;
 // means keys are rows 0 .. kv_len - 1 of the cache
 int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
                      int64_t kv_sh, int64_t kv_sn, const int32_t* kv_idx, int64_t idx_sb, int64_t idx_sh,
-                     int kv_rows, const int32_t* kv_len, int max_kv_len, int dtype, int batch, int nq, int Hq,
-                     int Hkv, int D, float scale, int causal_tail, float* out, float* lse, int num_splits, void* ws,
-                     size_t ws_bytes, void* stream) {
-  if (dtype != SVLM_BF16) return fail(SVLM_E_UNSUPPORTED, "%s: only SVLM_BF16 operands are supported", name);
+                     int kv_rows, const int32_t* kv_len, int64_t len_sb, int64_t len_sh, int max_kv_len, int dtype,
+                     int batch, int nq, int Hq, int Hkv, int D, float scale, int causal_tail, float* out, float* lse,
+                     int num_splits, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != SVLM_BF16 && dtype != SVLM_F32) return fail(SVLM_E_UNSUPPORTED, "%s: unknown dtype %d", name, dtype);
   if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", name, D);
+  const int epc = (dtype == SVLM_F32) ? 4 : 8;  // elements per 16 bytes
   if (!q || !k || !v || !kv_len || !out) return fail(SVLM_E_INVALID, "%s: null pointer", name);
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || max_kv_len < 1)
     return fail(SVLM_E_INVALID, "%s: batch, nq, Hq, Hkv and the key count bound must be >= 1", name);
@@ -765,15 +767,46 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite and > 0", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(SVLM_E_INVALID, "%s: q, k, v, out must be 16-byte aligned", name);
-  if (kv_sn < D || kv_sn % 8 || kv_sh % 8 || kv_sb % 8 || kv_sh < 0 || kv_sb < 0)
-    return fail(SVLM_E_INVALID, "%s: KV strides must be multiples of 8 elements with kv_sn >= D", name);
-  if (q_sb % 8 || (batch > 1 && q_sb < (int64_t)nq * Hq * D))
-    return fail(SVLM_E_INVALID, "%s: q batch stride must be a multiple of 8 and >= nq*Hq*D", name);
+  if (kv_sn < D || kv_sn % epc || kv_sh % epc || kv_sb % epc || kv_sh < 0 || kv_sb < 0)
+    return fail(SVLM_E_INVALID, "%s: KV strides must be multiples of 16 bytes with kv_sn >= D", name);
+  if (q_sb % epc || (batch > 1 && q_sb < (int64_t)nq * Hq * D))
+    return fail(SVLM_E_INVALID, "%s: q batch stride must be a multiple of 16 bytes and >= nq*Hq*D", name);
   if (num_splits < 0) return fail(SVLM_E_INVALID, "%s: num_splits must be >= 0", name);
+  if (len_sb < 0 || len_sh < 0) return fail(SVLM_E_INVALID, "%s: length strides must be >= 0", name);
   if (kv_idx) {
-    if (kv_rows < 1 || (int64_t)kv_rows * kv_sn * 2 > INT32_MAX)
+    if (kv_rows < 1 || (dtype == SVLM_BF16 && (int64_t)kv_rows * kv_sn * 2 > INT32_MAX))
       return fail(SVLM_E_INVALID, "%s: kv_rows must be >= 1 with kv_rows * kv_sn * 2 < 2^31", name);
     if (idx_sb < 0 || idx_sh < 0) return fail(SVLM_E_INVALID, "%s: index strides must be >= 0", name);
+  }
+  if (dtype == SVLM_F32) {
+    // plain fp32 rows, one wave each; no split state, so no workspace
+    AttnF32Args f;
+    f.q = (const float*)q;
+    f.q_sb = q_sb;
+    f.k = (const float*)k;
+    f.v = (const float*)v;
+    f.kv_sb = kv_sb;
+    f.kv_sh = kv_sh;
+    f.kv_sn = kv_sn;
+    f.kv_len = kv_len;
+    f.len_sb = len_sb;
+    f.len_sh = len_sh;
+    f.max_kv_len = max_kv_len;
+    f.kv_idx = kv_idx;
+    f.idx_sb = idx_sb;
+    f.idx_sh = idx_sh;
+    f.kv_rows = kv_rows;
+    f.batch = batch;
+    f.nq = nq;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.D = D;
+    f.scale = scale;
+    f.causal = causal_tail;
+    f.out = out;
+    f.lse = lse;
+    launch_attn_f32(f, (hipStream_t)stream);
+    return check_launch(name);
   }
   // buffer-descriptor ranges and offsets are 32-bit: one batch entry's
   // queries, and one split's keys (plus the blocks staged past its end)
@@ -797,6 +830,8 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   a.kv_sh = kv_sh;
   a.kv_sn = kv_sn;
   a.kv_len = kv_len;
+  a.len_sb = len_sb;
+  a.len_sh = len_sh;
   a.max_kv_len = max_kv_len;
   a.batch = batch;
   a.nq = nq;
@@ -840,7 +875,7 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
                                 int batch, int nq, int Hq, int Hkv, int D, float scale, int causal_tail,
                                 float* out, float* lse, int num_splits, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return decode_attn_impl("svlm_decode_attn", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, nullptr, 0, 0, 0, kv_len,
+  return decode_attn_impl("svlm_decode_attn", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, nullptr, 0, 0, 0, kv_len, 1, 0,
                           max_kv_len, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse, num_splits, ws,
                           ws_bytes, stream);
 }
@@ -854,12 +889,12 @@ extern "C" size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, 
 
 extern "C" int svlm_decode_attn_indexed(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
                                         int64_t kv_sh, int64_t kv_sn, int kv_rows, const int32_t* kv_idx,
-                                        int64_t idx_sb, int64_t idx_sh, const int32_t* n_idx, int max_n_idx,
-                                        int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                                        int64_t idx_sb, int64_t idx_sh, const int32_t* n_idx, int64_t n_sb,
+                                        int64_t n_sh, int max_n_idx, int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
                                         int causal_tail, float* out, float* lse, int num_splits, void* ws,
                                         size_t ws_bytes, void* stream) {
   if (!kv_idx) return fail(SVLM_E_INVALID, "svlm_decode_attn_indexed: null index list");
   return decode_attn_impl("svlm_decode_attn_indexed", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, kv_idx, idx_sb, idx_sh,
-                          kv_rows, n_idx, max_n_idx, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse,
+                          kv_rows, n_idx, n_sb, n_sh, max_n_idx, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse,
                           num_splits, ws, ws_bytes, stream);
 }

@@ -614,7 +614,8 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
                           int dtype, int T, int n_ctx, int q_pos0, int vis_start, int n_vis, int Hq, int Hkv, int D,
                           float scale, int agg, float alpha, float beta, float* out, void* ws, size_t ws_bytes,
                           void* stream) {
-  if (dtype != SVLM_BF16) return fail(SVLM_E_UNSUPPORTED, "svlm_score: only SVLM_BF16 operands are supported");
+  if (dtype != SVLM_BF16 && dtype != SVLM_F32) return fail(SVLM_E_UNSUPPORTED, "svlm_score: unknown dtype %d", dtype);
+  const int epc = (dtype == SVLM_F32) ? 4 : 8;  // elements per 16 bytes
   if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "svlm_score: D must be 64 or 128 (got %d)", D);
   if (T < 1 || T > 128) return fail(SVLM_E_UNSUPPORTED, "svlm_score: 1 <= T <= 128 text queries supported (got %d)", T);
   if (!q_text || !k || !out) return fail(SVLM_E_INVALID, "svlm_score: null pointer");
@@ -628,8 +629,39 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
     return fail(SVLM_E_INVALID, "svlm_score: unknown aggregation %d", agg);
   if (!std::isfinite(alpha) || !std::isfinite(beta)) return fail(SVLM_E_INVALID, "svlm_score: alpha, beta must be finite");
   if (!aligned16(q_text) || !aligned16(k)) return fail(SVLM_E_INVALID, "svlm_score: q_text and k must be 16-byte aligned");
-  if (q_st % 8 || q_sh % 8 || k_sh % 8 || k_sn % 8 || k_sn < D || q_st < 0 || q_sh < 0 || k_sh < 0)
-    return fail(SVLM_E_INVALID, "svlm_score: strides must be non-negative multiples of 8 elements, k_sn >= D");
+  if (q_st % epc || q_sh % epc || k_sh % epc || k_sn % epc || k_sn < D || q_st < 0 || q_sh < 0 || k_sh < 0)
+    return fail(SVLM_E_INVALID, "svlm_score: strides must be non-negative multiples of 16 bytes, k_sn >= D");
+  if (dtype == SVLM_F32) {
+    // plain fp32 path: row log-sum-exp into the workspace, then the
+    // aggregated column means straight into out
+    const size_t need = svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis);
+    if (!ws || ws_bytes < need)
+      return fail(SVLM_E_WORKSPACE, "svlm_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_score: workspace must be 16-byte aligned");
+    ScoreF32Args f;
+    f.q = (const float*)q_text;
+    f.q_st = q_st;
+    f.q_sh = q_sh;
+    f.k = (const float*)k;
+    f.k_sh = k_sh;
+    f.k_sn = k_sn;
+    f.T = T;
+    f.q_pos0 = q_pos0;
+    f.vis_start = vis_start;
+    f.n_vis = n_vis;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.D = D;
+    f.scale = scale;
+    f.lse = (float*)ws;
+    f.agg = agg;
+    f.alpha = alpha;
+    f.beta = beta;
+    f.out = out;
+    const int rows = (agg == SVLM_AGG_QHEAD) ? Hq : (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
+    launch_score_f32(f, rows, (hipStream_t)stream);
+    return check_launch("svlm_score");
+  }
   // buffer-descriptor ranges and offsets are 32-bit: one head's text queries,
   // and one KV head's keys (plus the tiles staged past a split's end)
   if (((int64_t)(T - 1) * q_st + D) * 2 > INT32_MAX || ((int64_t)n_ctx + 1024) * k_sn * 2 > INT32_MAX)

@@ -19,6 +19,43 @@ int num_cus();                                     // compute units of the curre
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
+// fp32 operands (SVLM_F32): plain vector-ALU kernels in f32_path.hip
+// ---------------------------------------------------------------------------
+struct AttnF32Args {
+  const float* q;
+  int64_t q_sb;
+  const float* k;
+  const float* v;
+  int64_t kv_sb, kv_sh, kv_sn;
+  const int32_t* kv_len;  // key count of (b, g) at kv_len[b * len_sb + g * len_sh]
+  int64_t len_sb, len_sh;
+  int max_kv_len;
+  const int32_t* kv_idx;  // nullptr: keys are cache rows 0 .. n - 1
+  int64_t idx_sb, idx_sh;
+  int kv_rows;
+  int batch, nq, Hq, Hkv, D;
+  float scale;
+  int causal;
+  float* out;
+  float* lse;
+};
+void launch_attn_f32(const AttnF32Args& a, hipStream_t st);
+
+struct ScoreF32Args {
+  const float* q;
+  int64_t q_st, q_sh;
+  const float* k;
+  int64_t k_sh, k_sn;
+  int T, q_pos0, vis_start, n_vis, Hq, Hkv, D;
+  float scale;
+  float* lse;  // workspace [Hq][T], natural log
+  int agg;
+  float alpha, beta;
+  float* out;
+};
+void launch_score_f32(const ScoreF32Args& a, int rows, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // device side: vector types for the bf16 matrix-core builtins
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;

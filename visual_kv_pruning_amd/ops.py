@@ -34,6 +34,23 @@ def _bf16(*ts):
             raise ValueError("the last (head-dim) axis must be contiguous")
 
 
+_DTYPES = {torch.bfloat16: L.SVLM_BF16, torch.float32: L.SVLM_F32}
+
+
+def _operands(*ts) -> int:
+    """Attention operands: all bf16 (the matrix-core kernels) or all fp32 (the
+    plain fp32 kernels), head-dim axis contiguous.  Returns the svlm dtype code."""
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"expected bfloat16 or float32 operands, got {dt}")
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError(f"operands must share one dtype ({dt} and {t.dtype})")
+        if t.stride(-1) != 1:
+            raise ValueError("the last (head-dim) axis must be contiguous")
+    return _DTYPES[dt]
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -58,9 +75,10 @@ def score_workspace_bytes(T: int, Hq: int, Hkv: int, q_pos0: int, n_vis: int) ->
 def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_start: int = 0,
           agg: str = "all", alpha: float = 1.0, beta: float = 0.0, out: torch.Tensor | None = None,
           scale: float | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
-    """Mean text->visual attention of one layer.  q_text [T][Hq][D], k [Hkv][n_ctx][D] (bf16)."""
+    """Mean text->visual attention of one layer.  q_text [T][Hq][D], k [Hkv][n_ctx][D]
+    (both bf16, or both fp32 for the plain fp32 kernels)."""
     _dev(q_text, k, out, ws)
-    _bf16(q_text, k)
+    dtype = _operands(q_text, k)
     T, Hq, D = q_text.shape
     Hkv, n_ctx, Dk = k.shape
     if Dk != D:
@@ -78,7 +96,7 @@ def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_st
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     L.call("svlm_score", q_text.data_ptr(), q_text.stride(0), q_text.stride(1), k.data_ptr(), k.stride(0),
-           k.stride(1), L.SVLM_BF16, T, n_ctx, q_pos0, vis_start, n_vis, Hq, Hkv, D, float(scale), _AGG[agg],
+           k.stride(1), dtype, T, n_ctx, q_pos0, vis_start, n_vis, Hq, Hkv, D, float(scale), _AGG[agg],
            float(alpha), float(beta), out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
     return out
 
@@ -99,6 +117,8 @@ def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: i
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be fp32 [R][n_vis] with contiguous rows")
     R, n = scores.shape
+    if F * H * W != n:
+        raise ValueError(f"F*H*W = {F * H * W} must equal the row length {n}")
     dev = scores.device
     kept = torch.empty(R, budget, dtype=torch.int32, device=dev)
     n1 = torch.empty(R, dtype=torch.int32, device=dev)
@@ -116,9 +136,9 @@ def select(scores: torch.Tensor, F: int, H: int, W: int, top_p: float, budget: i
 # ---------------------------------------------------------------------------
 def gather_kv(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, tail_start: int = 0, n_tail: int = 0,
               k_dst: torch.Tensor | None = None, v_dst: torch.Tensor | None = None):
-    """k, v [Hkv][N][D] bf16; idx [n_idx] or [Hkv][n_idx] int32 -> compact [Hkv][n_idx+n_tail][D]."""
+    """k, v [Hkv][N][D] bf16 (or fp32); idx [n_idx] or [Hkv][n_idx] int32 -> compact [Hkv][n_idx+n_tail][D]."""
     _dev(k, v, idx, k_dst, v_dst)
-    _bf16(k, v)
+    dtype = _operands(k, v)
     if k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("k and v must have the same shape and strides")
     if idx.dtype != torch.int32 or idx.stride(-1) != 1:
@@ -132,7 +152,8 @@ def gather_kv(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, tail_start: i
     if k_dst is None:
         k_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
         v_dst = torch.empty(Hkv, n_out, D, dtype=k.dtype, device=k.device)
-    _bf16(k_dst, v_dst)
+    if _operands(k, v, k_dst, v_dst) != dtype:
+        raise TypeError("destination dtype differs")
     if k_dst.shape != v_dst.shape or k_dst.stride() != v_dst.stride():
         raise ValueError("k_dst and v_dst must have the same shape and strides")
     if k_dst.dim() != 3 or k_dst.shape[0] != Hkv or k_dst.shape[1] < n_out or k_dst.shape[2] != D:
@@ -141,7 +162,7 @@ def gather_kv(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, tail_start: i
         raise ValueError("2-D idx must be [Hkv][n_idx]")
     L.call("svlm_gather_kv", k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1), N, idx.data_ptr(), idx_sh,
            n_idx, tail_start, n_tail, k_dst.data_ptr(), v_dst.data_ptr(), k_dst.stride(0), k_dst.stride(1), Hkv, D,
-           L.SVLM_BF16, _stream())
+           dtype, _stream())
     return k_dst, v_dst
 
 
@@ -153,9 +174,11 @@ def decode_attn_workspace_bytes(batch, nq, Hq, Hkv, D, max_kv_len, num_splits=0)
 def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor, causal_tail: bool,
                 scale: float | None = None, num_splits: int = 0, out: torch.Tensor | None = None,
                 lse: torch.Tensor | None = None, ws: torch.Tensor | None = None, want_lse: bool = True):
-    """q [B][nq][Hq][D]; k, v [B][Hkv][N][D] or [Hkv][N][D]; kv_len int32 [B] -> (out fp32, lse fp32)."""
+    """q [B][nq][Hq][D]; k, v [B][Hkv][N][D] or [Hkv][N][D]; kv_len int32 [B] -> (out fp32, lse fp32).
+
+    q, k, v are all bf16 (matrix-core kernels) or all fp32 (plain fp32 kernels)."""
     _dev(q, k, v, kv_len, out, lse, ws)
-    _bf16(q, k, v)
+    dtype = _operands(q, k, v)
     B, nq, Hq, D = q.shape
     if q[0].stride() != (Hq * D, D, 1):
         raise ValueError("q must be contiguous inside each batch entry")
@@ -166,8 +189,11 @@ def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch
         Hkv, N, _ = k.shape
         kv_sh, kv_sn = k.stride(0), k.stride(1)
     else:
+        if k.dim() != 4 or k.shape[0] not in (1, B):
+            raise ValueError(f"4-D k and v must be [B={B} or 1][Hkv][N][D]")
         Hkv, N = k.shape[1], k.shape[2]
-        kv_sb, kv_sh, kv_sn = k.stride(0) if B > 1 else 0, k.stride(1), k.stride(2)
+        # a batch axis of 1 is shared by every batch entry (batch stride 0)
+        kv_sb, kv_sh, kv_sn = k.stride(0) if k.shape[0] > 1 else 0, k.stride(1), k.stride(2)
     q_sb = q.stride(0) if B > 1 else nq * Hq * D
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must have identical shapes and strides")
@@ -180,13 +206,13 @@ def decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_len: torch
         lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_out(lse, (B, nq, Hq), torch.float32, "lse")
-    need = decode_attn_workspace_bytes(B, nq, Hq, Hkv, D, N, num_splits)
+    need = decode_attn_workspace_bytes(B, nq, Hq, Hkv, D, N, num_splits) if dtype == L.SVLM_BF16 else 0
     if ws is None and need > 0:
         ws = _ws(need, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     L.call("svlm_decode_attn", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn,
-           kv_len.data_ptr(), N, L.SVLM_BF16, B, nq, Hq, Hkv, D, float(scale), 1 if causal_tail else 0,
+           kv_len.data_ptr(), N, dtype, B, nq, Hq, Hkv, D, float(scale), 1 if causal_tail else 0,
            out.data_ptr(), lse.data_ptr() if lse is not None else None, num_splits,
            ws.data_ptr() if ws is not None else None, _nbytes(ws), _stream())
     return out, lse
@@ -203,10 +229,11 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
     """Decode attention over cache rows named by kv_idx, read in place.
 
     q [B][nq][Hq][D]; k, v [B][Hkv][rows][D] or [Hkv][rows][D]; kv_idx int32
-    [n] (one list), [Hkv][n] (per head) or [B][Hkv][n]; n_idx int32 [B] (list
-    lengths) -> (out fp32, lse fp32)."""
+    [n] (one list), [Hkv][n] (per head) or [B][Hkv][n]; n_idx int32 [B] (one
+    length per batch entry) or [B][Hkv] (ragged per-head lengths) -> (out
+    fp32, lse fp32).  q, k, v all bf16, or all fp32."""
     _dev(q, k, v, kv_idx, n_idx, out, lse, ws)
-    _bf16(q, k, v)
+    dtype = _operands(q, k, v)
     B, nq, Hq, D = q.shape
     if q[0].stride() != (Hq * D, D, 1):
         raise ValueError("q must be contiguous inside each batch entry")
@@ -217,8 +244,11 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
         Hkv, rows, _ = k.shape
         kv_sh, kv_sn = k.stride(0), k.stride(1)
     else:
+        if k.dim() != 4 or k.shape[0] not in (1, B):
+            raise ValueError(f"4-D k and v must be [B={B} or 1][Hkv][rows][D]")
         Hkv, rows = k.shape[1], k.shape[2]
-        kv_sb, kv_sh, kv_sn = k.stride(0) if B > 1 else 0, k.stride(1), k.stride(2)
+        # a batch axis of 1 is shared by every batch entry (batch stride 0)
+        kv_sb, kv_sh, kv_sn = k.stride(0) if k.shape[0] > 1 else 0, k.stride(1), k.stride(2)
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must have identical shapes and strides")
     if kv_idx.dtype != torch.int32 or kv_idx.stride(-1) != 1:
@@ -234,8 +264,14 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
             raise ValueError("3-D kv_idx must be [B][Hkv][n]")
         idx_sb, idx_sh = kv_idx.stride(0), kv_idx.stride(1)
     max_n = kv_idx.shape[-1]
-    if n_idx.dtype != torch.int32 or n_idx.numel() != B:
-        raise ValueError("n_idx must be int32 [B]")
+    if n_idx.dtype != torch.int32 or not n_idx.is_contiguous():
+        raise ValueError("n_idx must be contiguous int32")
+    if tuple(n_idx.shape) == (B, Hkv) and Hkv > 1:
+        n_sb, n_sh = Hkv, 1
+    elif n_idx.numel() == B:
+        n_sb, n_sh = 1, 0
+    else:
+        raise ValueError(f"n_idx must be int32 [B={B}] or [B][Hkv={Hkv}]")
     q_sb = q.stride(0) if B > 1 else nq * Hq * D
     if out is None:
         out = torch.empty(B, nq, Hq, D, dtype=torch.float32, device=q.device)
@@ -244,13 +280,13 @@ def decode_attn_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
         lse = torch.empty(B, nq, Hq, dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_out(lse, (B, nq, Hq), torch.float32, "lse")
-    need = decode_attn_indexed_workspace_bytes(B, nq, Hq, Hkv, D, max_n, num_splits)
+    need = decode_attn_indexed_workspace_bytes(B, nq, Hq, Hkv, D, max_n, num_splits) if dtype == L.SVLM_BF16 else 0
     if ws is None and need > 0:
         ws = _ws(need, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     L.call("svlm_decode_attn_indexed", q.data_ptr(), q_sb, k.data_ptr(), v.data_ptr(), kv_sb, kv_sh, kv_sn, rows,
-           kv_idx.data_ptr(), idx_sb, idx_sh, n_idx.data_ptr(), max_n, L.SVLM_BF16, B, nq, Hq, Hkv, D,
+           kv_idx.data_ptr(), idx_sb, idx_sh, n_idx.data_ptr(), n_sb, n_sh, max_n, dtype, B, nq, Hq, Hkv, D,
            float(scale), 1 if causal_tail else 0, out.data_ptr(), lse.data_ptr() if lse is not None else None,
            num_splits, ws.data_ptr() if ws is not None else None, _nbytes(ws), _stream())
     return out, lse

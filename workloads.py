@@ -196,16 +196,18 @@ def prefill_layer(cfg: Config, layer: int, round_bf16: bool = True) -> Prefill:
 # ---------------------------------------------------------------------------
 
 
-def decode_queries(cfg: Config, layer: int, nq: int, batch: int = 1, extra: int = 0) -> np.ndarray:
-    """[B][nq][Hq][D] bf16-valued fp32 queries."""
+def decode_queries(cfg: Config, layer: int, nq: int, batch: int = 1, extra: int = 0,
+                   round_bf16: bool = True) -> np.ndarray:
+    """[B][nq][Hq][D] bf16-valued fp32 queries (plain fp32 with round_bf16=False)."""
     q = _normal(rng_for(cfg.index, "q_dec", layer, extra), (batch, nq, cfg.hq, cfg.d))
-    return bf16_round(q)
+    return bf16_round(q) if round_bf16 else q
 
 
-def new_kv(cfg: Config, layer: int, n_new: int, extra: int = 0):
+def new_kv(cfg: Config, layer: int, n_new: int, extra: int = 0, round_bf16: bool = True):
     """[Hkv][n_new][D] keys and values of freshly decoded tokens."""
-    k = bf16_round(_normal(rng_for(cfg.index, "k_new", layer, extra), (cfg.hkv, n_new, cfg.d)))
-    v = bf16_round(_normal(rng_for(cfg.index, "v_new", layer, extra), (cfg.hkv, n_new, cfg.d)))
+    rnd = bf16_round if round_bf16 else (lambda a: a)
+    k = rnd(_normal(rng_for(cfg.index, "k_new", layer, extra), (cfg.hkv, n_new, cfg.d)))
+    v = rnd(_normal(rng_for(cfg.index, "v_new", layer, extra), (cfg.hkv, n_new, cfg.d)))
     return k, v
 
 

@@ -219,6 +219,32 @@ int svlm_decode_attn(const void* q, int64_t q_sb,
                      int num_splits, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * svlm_decode_attn_noalloc - svlm_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, with the
+ * split-K partial state kept in a static device array of
+ * SVLM_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends.  The call allocates nothing.
+ *
+ * Arguments are svlm_decode_attn's without the workspace.  A call whose
+ * svlm_decode_attn_workspace(...) size exceeds SVLM_NOALLOC_SCRATCH_BYTES
+ * returns SVLM_E_UNSUPPORTED before enqueueing anything (16 MiB covers dense
+ * verify of 10 queries over 141194 keys at 28 q / 4 KV heads, which needs
+ * about 8 MB).  The scratch needs no initial contents.  All calls on one
+ * device share its scratch: calls that may overlap in time on one device
+ * (different streams, or graph replays running concurrently) race and must
+ * not be issued.  The array's device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call with that device current; a failure
+ * there is SVLM_E_HIP.
+ * ------------------------------------------------------------------------ */
+#define SVLM_NOALLOC_SCRATCH_BYTES (16u << 20)
+int svlm_decode_attn_noalloc(const void* q, int64_t q_sb,
+                             const void* k, const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                             const int32_t* kv_len, int max_kv_len,
+                             int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                             int causal_tail, float* out, float* lse, int num_splits, void* stream);
+
+/* ------------------------------------------------------------------------
  * svlm_decode_attn_indexed - svlm_decode_attn over keys named by an index
  * list, read in place from the full cache (the gather fused into the draft).
  * [StD-sel] ("dual-module architecture": the sparse draft reads only the

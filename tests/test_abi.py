@@ -190,3 +190,15 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     args[16] = 2
     args[1] = 1 << 27                        # one head's queries past a 32-bit buffer range
     assert lib.svlm_score(*args) == L.SVLM_E_UNSUPPORTED
+
+
+def test_noalloc_refuses_state_beyond_its_scratch_on_the_host(lib):
+    """The no-allocation attention call checks its split-K state against the
+    static scratch before anything else touches the device."""
+    fake = C.c_void_p(4096)
+    need = lib.svlm_decode_attn_workspace(1, 64, 64, 8, 128, 1 << 20, 256)
+    assert need > L.SVLM_NOALLOC_SCRATCH_BYTES
+    st = lib.svlm_decode_attn_noalloc(fake, 64 * 64 * 128, fake, fake, 0, 128 << 20, 128, fake, 1 << 20,
+                                      L.SVLM_BF16, 1, 64, 64, 8, 128, C.c_float(0.1), 1, fake, fake, 256, None)
+    assert st == L.SVLM_E_UNSUPPORTED
+    assert b"scratch" in lib.svlm_last_error()

@@ -15,6 +15,7 @@ SVLM_OK, SVLM_E_INVALID, SVLM_E_UNSUPPORTED, SVLM_E_WORKSPACE, SVLM_E_HIP = rang
 SVLM_BF16, SVLM_F32 = 0, 1
 SVLM_AGG_QHEAD, SVLM_AGG_KVHEAD, SVLM_AGG_ALL = 0, 1, 2
 SVLM_VERIFY_GREEDY, SVLM_VERIFY_REJECT = 0, 1
+SVLM_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 vp, i64, i32, f32, f64, sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_double, C.c_size_t
 
@@ -32,6 +33,8 @@ SIGNATURES = {
     "svlm_decode_attn_workspace": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "svlm_decode_attn": (i32, [vp, i64, vp, vp, i64, i64, i64, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                vp, vp, i32, vp, sz, vp]),
+    "svlm_decode_attn_noalloc": (i32, [vp, i64, vp, vp, i64, i64, i64, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                       i32, vp, vp, i32, vp]),
     "svlm_decode_attn_indexed_workspace": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "svlm_decode_attn_indexed": (i32, [vp, i64, vp, vp, i64, i64, i64, i32, vp, i64, i64, vp, i64, i64, i32, i32,
                                        i32, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp, sz, vp]),

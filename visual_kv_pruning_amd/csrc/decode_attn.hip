@@ -32,6 +32,8 @@
 //    output) that a second kernel merges in split order.  Deterministic.
 #include <cmath>
 #include <cstdio>
+#include <mutex>
+#include <vector>
 
 #include "svlm_internal.h"
 
@@ -897,4 +899,57 @@ extern "C" int svlm_decode_attn_indexed(const void* q, int64_t q_sb, const void*
   return decode_attn_impl("svlm_decode_attn_indexed", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, kv_idx, idx_sb, idx_sh,
                           kv_rows, n_idx, n_sb, n_sh, max_n_idx, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse,
                           num_splits, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// svlm_decode_attn_noalloc: svlm_decode_attn with the split-K partial state in
+// a static device array instead of a caller workspace, for callers that
+// cannot allocate (graph capture, serving loops).  Each device holds its own
+// copy of the array; its address is looked up once per device.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = (size_t)SVLM_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device: the device address of `scratch`
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVLM_E_HIP, "svlm_decode_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SVLM_E_HIP, "svlm_decode_attn_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVLM_OK;
+}
+}  // namespace
+
+extern "C" int svlm_decode_attn_noalloc(const void* q, int64_t q_sb, const void* k, const void* v, int64_t kv_sb,
+                                        int64_t kv_sh, int64_t kv_sn, const int32_t* kv_len, int max_kv_len,
+                                        int dtype, int batch, int nq, int Hq, int Hkv, int D, float scale,
+                                        int causal_tail, float* out, float* lse, int num_splits, void* stream) {
+  size_t need = 0;
+  if (dtype == SVLM_BF16) {
+    need = svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
+    if (need > kScratchBytes)
+      return fail(SVLM_E_UNSUPPORTED,
+                  "svlm_decode_attn_noalloc: this call needs %zu bytes of split-K state; the static scratch "
+                  "holds %zu (use svlm_decode_attn with a workspace, or fewer splits)", need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = scratch_address(&ws);
+    if (st != SVLM_OK) return st;
+  }
+  return decode_attn_impl("svlm_decode_attn_noalloc", q, q_sb, k, v, kv_sb, kv_sh, kv_sn, nullptr, 0, 0, 0, kv_len,
+                          1, 0, max_kv_len, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse, num_splits,
+                          ws, need > 0 ? kScratchBytes : 0, stream);
 }

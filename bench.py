@@ -283,27 +283,16 @@ def main():
     # beside the workload above, not part of `value`.
     hour = measure_hour_shape(torch, ops, dev, g, args.steps)
 
-    # (3) an achievable streaming rate on this part: a plain device copy of the
-    # 80-layer K cache (read + write bytes), timed the same way
-    copy_dst = torch.empty_like(K)
-    copy_dst.copy_(K)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    copy_dst.copy_(K)
-    b.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * K.numel() * K.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
-    del copy_dst
-    # and a read-only pass: torch's sum over the same 4.1 GB (reads; a few bytes written)
-    K.sum(dtype=torch.float32)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    K.sum(dtype=torch.float32)
-    b.record()
-    torch.cuda.synchronize()
-    read_gbs = K.numel() * K.element_size() / (a.elapsed_time(b) * 1e-3) / 1e9
+    # (3) what this chip gives a launch: the in-tree streaming read (the
+    # attention kernels' access pattern, nothing else) over the whole 80-layer
+    # cache in one launch, over one layer's worth (103.3 MB, the verify
+    # grid) per launch in a graph of 80 dependent launches, and an empty launch
+    achievable = measure_achievable(torch, ops, dev, kv, args.steps)
+
+    # (3b) the draft and dense verify at batch 2 .. 32 (independent sequences:
+    # the data-parallel axis), and the 7B and 32B shapes
+    batch_sweep = measure_batch_sweep(torch, ops, dev, g, args.steps)
+    other_shapes = measure_other_shapes(torch, ops, dev, g, args.steps)
 
     bytes_row = Hkv * D * 2 * 2                       # K + V bytes per key
     verify_bytes = N_full * bytes_row                 # per layer
@@ -376,14 +365,147 @@ def main():
             "what": "80 dense-verify and 80 draft launches overlapped on two streams (one graph, two branches); "
                     "decode_attn_us_per_step runs them one after the other"},
         "hour_shape": hour,
-        "achievable": {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
-                       "what": "device copy of the 80-layer K cache (4.1 GB), read + write bytes per second; "
-                               "torch sum over it, bytes read per second"},
+        "achievable": achievable,
+        "batch_sweep": batch_sweep,
+        "other_shapes": other_shapes,
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, N_full, N_draft, bytes_row, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_us(torch, fn, calls, reps):
+    """Per-call microseconds of the launch sequence fn() (calls launches),
+    captured once as a HIP graph and timed by events around `reps` replays."""
+    fn()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    gr.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gr.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * calls)
+
+
+def measure_achievable(torch, ops, dev, kv, steps):
+    """The streaming read of svlm_stream_read: the whole 80-layer K and V cache
+    in one launch; 103.3 MB per launch (two adjacent layers of K or of V, the
+    bytes of one dense-verify call) over the verify grid, 80 dependent launches
+    in a graph; and 80 empty launches (the per-launch floor)."""
+    sink = torch.empty(4096, dtype=torch.float32, device=dev)
+    whole = kv.view(-1)
+    nb_whole = whole.numel() * whole.element_size()
+    us_whole = graph_us(torch, lambda: ops.stream_read(whole, 2048, sink), 1, max(2, steps // 2))
+    L = kv.shape[1]
+    pairs = [kv[w, l:l + 2].reshape(-1) for w in range(2) for l in range(0, L - 1, 2)]
+    nb_pair = pairs[0].numel() * pairs[0].element_size()
+    us_pair = graph_us(torch, lambda: [ops.stream_read(t, 216, sink) for t in pairs], len(pairs), steps)
+    us_empty = graph_us(torch, lambda: [ops.stream_read(None, 1, sink) for _ in range(80)], 80, steps)
+    return {
+        "stream_read_whole": {"bytes": nb_whole, "us": round(us_whole, 1),
+                              "gbs": round(nb_whole / (us_whole * 1e-6) / 1e9, 1),
+                              "what": "one launch over the 80-layer K and V cache, 2048 workgroups"},
+        "stream_read_per_launch": {"bytes": nb_pair, "us_avg": round(us_pair, 3),
+                                   "gbs": round(nb_pair / (us_pair * 1e-6) / 1e9, 1),
+                                   "frac": round(nb_pair / (us_pair * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "what": "103.3 MB (one dense-verify call's bytes) per launch over 216 "
+                                           "workgroups, 80 dependent launches in a graph"},
+        "empty_launch_us": round(us_empty, 3),
+        "what": "svlm_stream_read: the attention kernels' read pattern (1 KB LDS-DMA transfers, 16 KB in "
+                "flight per wave) and nothing else",
+    }
+
+
+def measure_batch_sweep(torch, ops, dev, g, steps, layers=8):
+    """The 10% draft (2638 keys) and the dense verify (6 queries over 25222
+    keys) at the 72B shape for batches of independent sequences, rotating over
+    `layers` layer buffers: per-call time, GB/s and fraction of peak."""
+    cfg = W.C3
+    Hq, Hkv, D = cfg.hq, cfg.hkv, cfg.d
+    row = Hkv * D * 2 * 2
+    out = {}
+    for kind, nq, N, batches in (("draft_attn", 1, cfg.budget + cfg.n_text + 1, (1, 2, 4, 8, 16, 32)),
+                                 ("verify_attn", cfg.gamma_verify + 1, cfg.n_ctx + cfg.gamma_verify + 1, (1, 2, 4))):
+        res = {}
+        for B in batches:
+            kvb = torch.empty(2, layers, B, Hkv, N, D, dtype=torch.bfloat16, device=dev)
+            kvb.normal_(generator=g)
+            qb = torch.randn(layers, B, nq, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+            ob = torch.empty(B, nq, Hq, D, device=dev)
+            lb = torch.empty(B, nq, Hq, device=dev)
+            kl = torch.full((B,), N, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(256, ops.decode_attn_workspace_bytes(B, nq, Hq, Hkv, D, N)), dtype=torch.uint8,
+                             device=dev)
+            us = graph_us(torch, lambda: [ops.decode_attn(qb[l], kvb[0, l], kvb[1, l], kl, nq > 1, out=ob, lse=lb,
+                                                          ws=ws) for l in range(layers)], layers, steps)
+            nb = B * N * row
+            res[f"B{B}"] = {"us_avg": round(us, 3), "bytes": nb, "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                            "frac": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del kvb
+        out[kind] = res
+    out["what"] = ("72B shape, batches of independent sequences (one cache each); draft 1 query over 2638 keys, "
+                   "verify 6 queries over 25222 keys; 8 rotating layer buffers")
+    return out
+
+
+def measure_other_shapes(torch, ops, dev, g, steps):
+    """Dense verify, 10% draft and the score per layer at the Qwen2-VL-7B shape
+    (28 layers, 28 q / 4 KV heads, 8192 + 64 tokens, gamma 9) and the
+    Qwen2.5-VL-32B shape (64 layers, 40 q / 8 KV heads, 20736 + 96 tokens,
+    gamma 9), rotating over enough layers to exceed the Infinity Cache."""
+    out = {}
+    for cfg, layers in ((W.C2, 28), (W.C4, 16)):
+        Hq, Hkv, D, T, NV = cfg.hq, cfg.hkv, cfg.d, cfg.n_text, cfg.n_vis
+        nq = cfg.gamma_verify + 1
+        Nv = cfg.n_ctx + nq
+        Nd = cfg.budget + T + 1
+        row = Hkv * D * 2 * 2
+        kv = torch.empty(2, layers, Hkv, Nv, D, dtype=torch.bfloat16, device=dev)
+        kv.normal_(generator=g)
+        qv = torch.randn(layers, 1, nq, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+        qt = torch.randn(layers, T, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+        o = torch.empty(1, nq, Hq, D, device=dev)
+        lse = torch.empty(1, nq, Hq, device=dev)
+        klv = torch.tensor([Nv], dtype=torch.int32, device=dev)
+        kld = torch.tensor([Nd], dtype=torch.int32, device=dev)
+        wsv = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, nq, Hq, Hkv, D, Nv)), dtype=torch.uint8,
+                          device=dev)
+        wsd = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, Nd)), dtype=torch.uint8,
+                          device=dev)
+        # the draft reads the first Nd rows of each layer's cache (timing only)
+        us_v = graph_us(torch, lambda: [ops.decode_attn(qv[l], kv[0, l], kv[1, l], klv, True, out=o, lse=lse,
+                                                        ws=wsv) for l in range(layers)], layers, steps)
+        us_d = graph_us(torch, lambda: [ops.decode_attn(qv[l][:, :1], kv[0, l, :, :Nd], kv[1, l, :, :Nd], kld,
+                                                        False, out=o[:, :1], lse=lse[:, :1], ws=wsd)
+                                        for l in range(layers)], layers, steps)
+        rows_out = {"all": 1, "layer": 1, "layer_kvhead": Hkv}[cfg.rows]
+        agg = "kvhead" if cfg.rows == "layer_kvhead" else "all"
+        srow = torch.empty(rows_out, NV, device=dev)
+        wss = torch.empty(ops.score_workspace_bytes(T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
+        us_s = graph_us(torch, lambda: [ops.score(qt[l], kv[0, l, :, :NV + T], NV, NV, agg=agg, out=srow, ws=wss)
+                                        for l in range(layers)], layers, max(2, steps // 2))
+        flop = 2 * D * Hq * (T * NV + T * (T + 1) // 2) + 2 * D * Hq * T * NV
+        out[cfg.name] = {
+            "verify_attn": {"us_avg": round(us_v, 3), "bytes": Nv * row, "keys": Nv, "queries": nq,
+                            "gbs": round(Nv * row / (us_v * 1e-6) / 1e9, 1),
+                            "frac": round(Nv * row / (us_v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "draft_attn": {"us_avg": round(us_d, 3), "bytes": Nd * row, "keys": Nd,
+                           "gbs": round(Nd * row / (us_d * 1e-6) / 1e9, 1),
+                           "frac": round(Nd * row / (us_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "score": {"us_avg": round(us_s, 3), "flop": flop, "tflops": round(flop / (us_s * 1e-6) / 1e12, 1),
+                      "frac_bf16_peak": round(flop / (us_s * 1e-6) / 1e12 / 2500.0, 4)},
+            "layers_rotated": layers,
+        }
+        del kv
+    return out
 
 
 def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
@@ -487,14 +609,42 @@ def cpu_baseline(cfg, N_full, N_draft, bytes_row, budget_s):
         t_used += time.perf_counter() - t0
         done_bytes += (N_full + N_draft) * bytes_row
         layers += 1
+    # one layer on one thread
+    one_thread_s = None
+    try:
+        from threadpoolctl import threadpool_limits
+        k, v = W.random_kv(cfg.index, cfg.hkv, N_full, cfg.d, layer=0)
+        qv = W.decode_queries(cfg, 0, nqv)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.decode_attn(qv, k, v, [N_full], True)
+            oracle.decode_attn(qv[:, :1], k[:, :N_draft], v[:, :N_draft], [N_draft], False)
+            one_thread_s = time.perf_counter() - t0
+    except Exception:  # pragma: no cover
+        pass
     return {
         "value": round(done_bytes / t_used / 1e9, 3),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "one_layer_1thread_s": round(one_thread_s, 3) if one_thread_s is not None else None,
+        "one_layer_1thread_gbs": round((N_full + N_draft) * bytes_row / one_thread_s / 1e9, 4)
+        if one_thread_s else None,
         "sample": f"{layers} layer(s) of dense verify (6 queries x 25222 keys) + 10% draft (1 x 2638 keys), "
-                  f"64 q / 8 KV heads, fp64 NumPy, {t_used:.1f} s",
+                  f"64 q / 8 KV heads, fp64 NumPy, {t_used:.1f} s; per-step figures would be x80 extrapolations",
     }
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 if __name__ == "__main__":

@@ -325,6 +325,20 @@ int svlm_verify(int mode, int batch, int gamma, int V, const int32_t* draft_tok,
                 int32_t* n_accept, int32_t* next_tok,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * svlm_stream_read - measurement helper (not a step of the path): reads
+ * `bytes` of src once, in the decode-attention kernel's access pattern (1 KB
+ * LDS-DMA transfers per wave, nontemporal, 16 KB in flight per wave, four
+ * waves per workgroup), split over `workgroups` contiguous ranges of whole
+ * KB, and writes one float per workgroup to sink (device, `workgroups`
+ * floats): the float at byte 4096 * (ceil(ceil(n / 1024) / 4) - 1) of its
+ * n-byte range (the start of the first wave's last transfer).  Its time is
+ * the achievable streaming rate of a launch of that size, the reference
+ * beside the HBM peak for the attention calls.  bytes = 0 launches one empty
+ * workgroup: the floor of a dependent launch.  src 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+int svlm_stream_read(const void* src, int64_t bytes, int workgroups, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

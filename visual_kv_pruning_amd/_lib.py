@@ -42,6 +42,7 @@ SIGNATURES = {
     "svlm_uvprune_score": (i32, [vp, vp, i64, i32, vp, vp, i64, i32, i32, i32, f32, f32, vp, vp, sz, vp]),
     "svlm_verify_workspace": (sz, [i32, i32, i32]),
     "svlm_verify": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "svlm_stream_read": (i32, [vp, i64, i32, vp, vp]),
 }
 
 ABI_VERSION = 3  # SVLM_ABI_VERSION of include/svlm.h

@@ -354,3 +354,17 @@ def verify(mode: str, draft_tok: torch.Tensor, target: torch.Tensor, draft_prob:
            draft_prob.data_ptr() if draft_prob is not None else None, u.data_ptr() if u is not None else None,
            n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
     return n_acc, nxt
+
+
+# ---------------------------------------------------------------------------
+def stream_read(src: torch.Tensor | None, workgroups: int, sink: torch.Tensor) -> None:
+    """Measurement helper: read src once in the attention kernels' access
+    pattern over `workgroups` workgroups (src None: one empty workgroup)."""
+    _dev(src, sink)
+    if sink.dtype != torch.float32 or sink.numel() < workgroups:
+        raise ValueError("sink must be fp32 with at least `workgroups` elements")
+    nbytes = 0 if src is None else _nbytes(src)
+    if src is not None and not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    L.call("svlm_stream_read", src.data_ptr() if src is not None else None, nbytes, workgroups, sink.data_ptr(),
+           _stream())

@@ -320,6 +320,12 @@ def main():
         bytes=uv_bytes, gbs=round(uv_bytes / (per_us["uvprune_score"] * 1e-6) / 1e9, 1),
         what="UV-Prune score from layer-0 and layer-L hidden states (hidden 8192), once per prefill")
     kernels["score"].update(flop=score_flop, tflops=round(score_flop / (us_score * 1e-6) / 1e12, 1))
+    # acceptance: the gamma test probabilities, then the one row (p_n and q_n, or the bonus row p_gamma)
+    # the draw scans; latency-bound (two launches, dependent loads)
+    acc_bytes = 2 * V * 4
+    kernels["accept"].update(bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept"] * 1e-6) / 1e9, 1),
+                             what="rejection acceptance, gamma 5, V 152064: bytes = the two probability rows "
+                                  "the draw reads (p_n and q_n); two launches of dependent loads")
     kernels["gather"].update(bytes=2 * 2 * (B_keep + T) * Hkv * D * 2,
                              gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (per_us["gather"] * 1e-6) / 1e9, 1))
 
@@ -353,6 +359,10 @@ def main():
             "traffic": measured_traffic(),
             "kernel": "svlm_decode_attn dense verify call (split-K kernel + combine; 25222 keys x 8 KV heads "
                       "x 512 B = 103.3 MB per call)",
+            # the same bytes through svlm_stream_read (the attention read pattern and nothing else),
+            # one launch per 103.3 MB in a graph: what a launch of this size gets on this chip
+            "achievable_gbs": achievable["stream_read_per_launch"]["gbs"],
+            "frac_of_achievable": round(verify_gbs / achievable["stream_read_per_launch"]["gbs"], 4),
         },
         "kernels": kernels,
         "parallel_decoding": {

@@ -94,10 +94,14 @@ struct VRaw<4> { typedef u32x2 T; };
 // at D = 128, four at D = 64).  Measured on 103 MB verify calls: deeper rings
 // (32 KB per wave) queue more requests without raising the rate and end
 // slower (28.9 against 28.1 us per call).
+#ifndef SVLM_ATTN_RING_KB
+#define SVLM_ATTN_RING_KB 16
+#endif
 template <int D>
 constexpr int ring_depth() {
   constexpr int SLOT = 2 * kBlock * D * 2;  // bytes of one staged K + V block
-  return (16 * 1024 / SLOT) < 2 ? 2 : 16 * 1024 / SLOT;
+  constexpr int RING = SVLM_ATTN_RING_KB * 1024;
+  return (RING / SLOT) < 2 ? 2 : RING / SLOT;
 }
 
 // One workgroup = one (batch, KV head, key split, row chunk) with kWaves waves.

@@ -72,3 +72,30 @@ def test_noalloc_refuses_state_beyond_the_scratch():
                                       L.SVLM_BF16, 1, 64, 64, 8, 128, C.c_float(0.1), 1, fake, fake, 256, None)
     assert st == L.SVLM_E_UNSUPPORTED
     assert b"scratch" in lib.svlm_last_error()
+
+
+def test_noalloc_fp32_operands_need_no_scratch():
+    """fp32 operands use no split state: the no-allocation call gives the
+    workspace call's bits without touching the scratch."""
+    from visual_kv_pruning_amd import _lib as L
+    lib = L.load()
+    rng = np.random.default_rng(9)
+    nq, Hq, Hkv, D, N = 3, 8, 2, 64, 500
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+    q, k, v = f32(rng.standard_normal((1, nq, Hq, D))), f32(rng.standard_normal((Hkv, N, D))), \
+        f32(rng.standard_normal((Hkv, N, D)))
+    kl = torch.tensor([N], dtype=torch.int32, device="cuda:0")
+    outs = []
+    for name in ("svlm_decode_attn", "svlm_decode_attn_noalloc"):
+        o = torch.full((1, nq, Hq, D), float("nan"), device="cuda:0")
+        l = torch.full((1, nq, Hq), float("nan"), device="cuda:0")
+        args = [q.data_ptr(), nq * Hq * D, k.data_ptr(), v.data_ptr(), 0, k.stride(0), k.stride(1), kl.data_ptr(), N,
+                L.SVLM_F32, 1, nq, Hq, Hkv, D, C.c_float(0.125), 1, o.data_ptr(), l.data_ptr(), 0]
+        if name == "svlm_decode_attn":
+            args += [None, 0]
+        assert getattr(lib, name)(*args, torch.cuda.current_stream().cuda_stream) == L.SVLM_OK
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    log("noalloc case fp32 operands")
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert not torch.isnan(outs[0][0]).any()

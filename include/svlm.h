@@ -38,6 +38,10 @@
  *     svlm_last_error() gives a text (thread-local).  SVLM_E_HIP reports a
  *     launch error from the HIP runtime (including an earlier asynchronous
  *     fault surfacing at this launch).
+ *   - A call whose launch would pass the dispatch limits (2^31 work-items
+ *     along x, 2^16 workgroups along y and z) returns SVLM_E_UNSUPPORTED
+ *     instead of a truncated grid.  The *_workspace() queries take any int
+ *     sizes without overflow and return 0 for sizes that their call refuses.
  *   - Device data that the host cannot see (indices, lengths, scores) are
  *     preconditions, stated per call; kernels clamp them so that no access
  *     leaves the buffers, but results are unspecified when they are violated.

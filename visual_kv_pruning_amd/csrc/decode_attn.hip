@@ -680,7 +680,7 @@ void launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
 
 template <int D, int RB>
 void launch_rb(const AttnArgs& a, int batch, int row_chunks, hipStream_t st) {
-  dim3 grid((unsigned)(batch * a.Hkv * a.splits), (unsigned)row_chunks);
+  dim3 grid((unsigned)((int64_t)batch * a.Hkv * a.splits), (unsigned)row_chunks);
   if (a.kv_idx) attn_splitk<D, RB, ring_depth<D>(), true><<<grid, 64 * kWaves, 0, st>>>(a);
   else attn_splitk<D, RB, ring_depth<D>(), false><<<grid, 64 * kWaves, 0, st>>>(a);
 }
@@ -697,40 +697,49 @@ void launch_d(const AttnArgs& a, int rb, int batch, int row_chunks, hipStream_t 
 }
 
 struct Plan {
-  int rb, row_chunks, splits, keys_per_split;
+  int64_t rb, row_chunks, splits, keys_per_split;
 };
 
 constexpr int kMinStepsPerSplit = 2;  // shorter splits cost more in fixed latency than they add in parallelism
 
 // max_steps_per_split > 0 caps the split length (indexed keys: the split's
-// list is staged in LDS)
+// list is staged in LDS).  64-bit throughout: the workspace queries take any
+// int sizes, and plan_fits() decides what can be launched.
 Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int num_splits,
                int max_steps_per_split = 0) {
   Plan p;
-  const int rows = (Hq / Hkv) * nq;
-  const int max_rb = (D == 128 && max_kv_len < kLongContextKeys) ? kMaxRBShort : kMaxRB;
+  const int64_t rows = (int64_t)(Hq / Hkv) * nq;
+  const int64_t max_rb = (D == 128 && max_kv_len < kLongContextKeys) ? kMaxRBShort : kMaxRB;
   // row blocks per chunk: as few chunks as possible, then as few padded rows
-  const int chunks = (rows + max_rb * 16 - 1) / (max_rb * 16);
+  const int64_t chunks = (rows + max_rb * 16 - 1) / (max_rb * 16);
   p.rb = ((rows + chunks - 1) / chunks + 15) / 16;
   p.row_chunks = (rows + p.rb * 16 - 1) / (p.rb * 16);
-  const int steps = (max_kv_len + kStep - 1) / kStep;
-  int splits = num_splits;
+  const int64_t steps = ((int64_t)max_kv_len + kStep - 1) / kStep;
+  int64_t splits = num_splits;
   if (splits <= 0) {
     // Workgroups for about seven eighths of the compute units: the key loop
     // is bound by HBM bandwidth before every unit is busy, each extra split
     // adds partial state for the merge, and one workgroup past the chip
     // (one per CU) starts a second round.  No split shorter than
     // kMinStepsPerSplit steps.
-    const int units = std::max(1, batch * Hkv * p.row_chunks);
-    splits = std::max(1, (7 * num_cus() / 8 + units - 1) / units);
-    splits = std::min(splits, std::max(1, steps / kMinStepsPerSplit));
+    const int64_t units = std::max<int64_t>(1, mul_sat(mul_sat(batch, Hkv), p.row_chunks));
+    splits = std::max<int64_t>(1, (7 * num_cus() / 8 + units - 1) / units);
+    splits = std::min(splits, std::max<int64_t>(1, steps / kMinStepsPerSplit));
   }
-  splits = std::max(1, std::min(splits, steps));
+  splits = std::max<int64_t>(1, std::min(splits, steps));
   if (max_steps_per_split > 0) splits = std::max(splits, (steps + max_steps_per_split - 1) / max_steps_per_split);
-  const int steps_per_split = (steps + splits - 1) / splits;
+  const int64_t steps_per_split = (steps + splits - 1) / splits;
   p.keys_per_split = steps_per_split * kStep;
-  p.splits = (max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
+  p.splits = ((int64_t)max_kv_len + p.keys_per_split - 1) / p.keys_per_split;
   return p;
+}
+
+// the split-K pass and the merge both fit the dispatch limits
+bool plan_fits(const Plan& p, int batch, int Hq, int Hkv, int nq) {
+  const int64_t rows = (int64_t)(Hq / Hkv) * nq;
+  const int64_t units = mul_sat(batch, Hkv);
+  return grid_fits(mul_sat(units, p.splits), 64 * kWaves, p.row_chunks) &&
+         (p.splits <= 1 || grid_fits(mul_sat(units, (rows + kCombineRows - 1) / kCombineRows), 256));
 }
 
 // Workspace layout: the partial outputs, then the partial (max, sum) pairs.
@@ -769,6 +778,9 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || max_kv_len < 1)
     return fail(SVLM_E_INVALID, "%s: batch, nq, Hq, Hkv and the key count bound must be >= 1", name);
   if (Hq % Hkv) return fail(SVLM_E_INVALID, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
+  // one batch entry's queries span a 32-bit buffer range
+  if ((int64_t)nq * Hq > INT32_MAX / (2 * D))
+    return fail(SVLM_E_UNSUPPORTED, "%s: nq * Hq * D * 2 must be below 2^31", name);
   if (causal_tail != 0 && causal_tail != 1) return fail(SVLM_E_INVALID, "%s: causal_tail must be 0 or 1", name);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite and > 0", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -786,6 +798,8 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   }
   if (dtype == SVLM_F32) {
     // plain fp32 rows, one wave each; no split state, so no workspace
+    if (!grid_fits((int64_t)batch * nq * Hq, 64))
+      return fail(SVLM_E_UNSUPPORTED, "%s: batch * nq * Hq output rows exceed the launch limit", name);
     AttnF32Args f;
     f.q = (const float*)q;
     f.q_sb = q_sb;
@@ -814,12 +828,13 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
     launch_attn_f32(f, (hipStream_t)stream);
     return check_launch(name);
   }
-  // buffer-descriptor ranges and offsets are 32-bit: one batch entry's
-  // queries, and one split's keys (plus the blocks staged past its end)
-  if ((int64_t)nq * Hq * D * 2 > INT32_MAX)
-    return fail(SVLM_E_UNSUPPORTED, "%s: nq * Hq * D * 2 must be below 2^31", name);
+  // buffer-descriptor ranges and offsets are 32-bit: one split's keys (plus
+  // the blocks staged past its end)
   const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits, kv_idx ? kIdxMaxSteps : 0);
-  if (!kv_idx && ((int64_t)p.keys_per_split + 8 * kStep) * kv_sn * 2 > INT32_MAX)
+  if (!plan_fits(p, batch, Hq, Hkv, nq))
+    return fail(SVLM_E_UNSUPPORTED, "%s: %lld splits for %d sequences x %d KV heads exceed the launch limit", name,
+                (long long)p.splits, batch, Hkv);
+  if (!kv_idx && (p.keys_per_split + 8 * kStep) * kv_sn * 2 > INT32_MAX)
     return fail(SVLM_E_UNSUPPORTED, "%s: one key split spans %lld rows of %lld bytes; must stay below 2^31 bytes",
                 name, (long long)p.keys_per_split, (long long)(kv_sn * 2));
   const size_t need = ws_layout(p, batch, Hq, nq, D).total;
@@ -847,8 +862,8 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   a.rows = a.G * nq;
   a.c = scale * kLog2e;
   a.causal = causal_tail;
-  a.splits = p.splits;
-  a.keys_per_split = p.keys_per_split;
+  a.splits = (int)p.splits;
+  a.keys_per_split = (int)p.keys_per_split;
   a.out = out;
   a.lse = lse;
   a.kv_idx = kv_idx;
@@ -859,8 +874,8 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
   a.ws_o = ws ? (float*)((char*)ws + wl.o_off) : nullptr;
   a.ws_ml = ws ? (float*)((char*)ws + wl.ml_off) : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  if (D == 128) launch_d<128>(a, p.rb, batch, p.row_chunks, st);
-  else launch_d<64>(a, p.rb, batch, p.row_chunks, st);
+  if (D == 128) launch_d<128>(a, (int)p.rb, batch, (int)p.row_chunks, st);
+  else launch_d<64>(a, (int)p.rb, batch, (int)p.row_chunks, st);
   if (p.splits > 1) {
     if (D == 128) launch_combine<128>(a, batch, st);
     else launch_combine<64>(a, batch, st);
@@ -872,7 +887,9 @@ int decode_attn_impl(const char* name, const void* q, int64_t q_sb, const void* 
 extern "C" size_t svlm_decode_attn_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len,
                                              int num_splits) {
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_kv_len < 1) return 0;
+  if ((int64_t)nq * Hq > INT32_MAX / (2 * D)) return 0;  // refused by the call
   const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_kv_len, num_splits);
+  if (!plan_fits(p, batch, Hq, Hkv, nq)) return 0;
   return ws_layout(p, batch, Hq, nq, D).total;
 }
 
@@ -889,7 +906,9 @@ extern "C" int svlm_decode_attn(const void* q, int64_t q_sb, const void* k, cons
 extern "C" size_t svlm_decode_attn_indexed_workspace(int batch, int nq, int Hq, int Hkv, int D, int max_n_idx,
                                                      int num_splits) {
   if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || max_n_idx < 1) return 0;
+  if ((int64_t)nq * Hq > INT32_MAX / (2 * D)) return 0;
   const Plan p = make_plan(batch, nq, Hq, Hkv, D, max_n_idx, num_splits, kIdxMaxSteps);
+  if (!plan_fits(p, batch, Hq, Hkv, nq)) return 0;
   return ws_layout(p, batch, Hq, nq, D).total;
 }
 

@@ -168,10 +168,10 @@ void launch_attn_f32(const AttnF32Args& a, hipStream_t st) {
 void launch_score_f32(const ScoreF32Args& a, int rows, hipStream_t st) {
   const dim3 cols((unsigned)((a.n_vis + 255) / 256), (unsigned)rows);
   if (a.D == 128) {
-    score_f32_lse<128><<<(unsigned)(a.Hq * a.T), 64, 0, st>>>(a);
+    score_f32_lse<128><<<(unsigned)((int64_t)a.Hq * a.T), 64, 0, st>>>(a);
     score_f32_cols<128><<<cols, 256, 0, st>>>(a);
   } else {
-    score_f32_lse<64><<<(unsigned)(a.Hq * a.T), 64, 0, st>>>(a);
+    score_f32_lse<64><<<(unsigned)((int64_t)a.Hq * a.T), 64, 0, st>>>(a);
     score_f32_cols<64><<<cols, 256, 0, st>>>(a);
   }
 }

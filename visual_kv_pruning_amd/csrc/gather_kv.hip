@@ -54,7 +54,8 @@ extern "C" int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh
   const int epc = (dtype == SVLM_F32) ? 4 : 8;  // elements per 16 bytes
   if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "svlm_gather_kv: D must be 64 or 128 (got %d)", D);
   if (n_idx < 0 || n_tail < 0 || Hkv < 1 || n_src < 0) return fail(SVLM_E_INVALID, "svlm_gather_kv: negative size");
-  if (n_idx + n_tail == 0) return SVLM_OK;  // nothing to copy
+  if ((int64_t)n_idx + n_tail == 0) return SVLM_OK;  // nothing to copy
+  if ((int64_t)n_idx + n_tail > INT32_MAX) return fail(SVLM_E_UNSUPPORTED, "svlm_gather_kv: n_idx + n_tail >= 2^31");
   if (!k_src || !v_src || !k_dst || !v_dst) return fail(SVLM_E_INVALID, "svlm_gather_kv: null K/V pointer");
   if (n_idx > 0 && !idx) return fail(SVLM_E_INVALID, "svlm_gather_kv: null index list");
   if (idx_sh < 0) return fail(SVLM_E_INVALID, "svlm_gather_kv: idx_sh must be >= 0");
@@ -82,6 +83,8 @@ extern "C" int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh
   a.tail_start = tail_start;
   a.n_tail = n_tail;
   const int rpb = 256 / (D / epc);
+  if (!grid_fits((n + rpb - 1) / rpb, 256, Hkv, 2))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_gather_kv: %d rows x %d KV heads exceed the launch limit", n, Hkv);
   dim3 grid((unsigned)((n + rpb - 1) / rpb), (unsigned)Hkv, 2);
   hipStream_t st = (hipStream_t)stream;
   if (dtype == SVLM_F32) {

@@ -515,15 +515,15 @@ __global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
 }
 
 // (g, s) pairs in groups of 8 (one per XCD), times the head groups
-inline unsigned pass_blocks(int Hkv, int S, int HG) { return (unsigned)((Hkv * S + 7) / 8 * 8 * HG); }
+inline int64_t pass_blocks(int Hkv, int S, int HG) { return ((int64_t)Hkv * S + 7) / 8 * 8 * HG; }
 
 template <int D, int RB, int W>
 void launch_pass1(const ScoreArgs& a, hipStream_t st) {
-  score_pass1<D, RB, W, score_ring_depth<D, W>()><<<pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
+  score_pass1<D, RB, W, score_ring_depth<D, W>()><<<(unsigned)pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
 }
 template <int D, int RB, int W>
 void launch_pass2(const ScoreArgs& a, hipStream_t st) {
-  score_pass2<D, RB, W, score_ring_depth<D, W>()><<<pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
+  score_pass2<D, RB, W, score_ring_depth<D, W>()><<<(unsigned)pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
 }
 
 template <int D, int RB>
@@ -572,15 +572,14 @@ int pick_waves(int G, int cap) {
 
 // key splits so that there is about one workgroup per compute unit, with at
 // least 2 tiles per split; the split length is a whole number of tiles
-int pick_splits(int groups, int w, int keys, int* kps) {
-  (void)w;
-  const int target = std::max(1, num_cus());
-  int S = std::max(1, (target + groups - 1) / groups);
-  const int tiles = (keys + kTileKeys - 1) / kTileKeys;
-  S = std::max(1, std::min(S, tiles / 2));
-  const int per_tiles = (tiles + S - 1) / S;
-  *kps = per_tiles * kTileKeys;
-  return (keys + *kps - 1) / *kps;
+int pick_splits(int64_t groups, int64_t keys, int* kps) {
+  const int64_t target = std::max(1, num_cus());
+  int64_t S = std::max<int64_t>(1, (target + groups - 1) / groups);
+  const int64_t tiles = (keys + kTileKeys - 1) / kTileKeys;
+  S = std::max<int64_t>(1, std::min(S, tiles / 2));
+  const int64_t per_tiles = (tiles + S - 1) / S;
+  *kps = (int)(per_tiles * kTileKeys);
+  return (int)((keys + *kps - 1) / *kps);
 }
 
 struct Geometry {
@@ -591,10 +590,10 @@ Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
   const int G = Hq / Hkv;
   gm.W1 = pick_waves(G, 8);
   gm.HG1 = (G + gm.W1 - 1) / gm.W1;
-  gm.S1 = pick_splits(Hkv * gm.HG1, gm.W1, q_pos0 + T, &gm.kps1);
+  gm.S1 = pick_splits((int64_t)Hkv * gm.HG1, (int64_t)q_pos0 + T, &gm.kps1);
   gm.W2 = pick_waves(G, 4);
   gm.HG2 = (G + gm.W2 - 1) / gm.W2;
-  gm.S2 = pick_splits(Hkv * gm.HG2, gm.W2, n_vis, &gm.kps2);
+  gm.S2 = pick_splits((int64_t)Hkv * gm.HG2, n_vis, &gm.kps2);
   return gm;
 }
 
@@ -604,7 +603,7 @@ Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
 using namespace svlm;
 
 extern "C" size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
-  if (T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || q_pos0 < 0 || n_vis < 1) return 0;
+  if (T < 1 || T > 128 || Hq < 1 || Hkv < 1 || Hq % Hkv || q_pos0 < 0 || n_vis < 1 || n_vis > (1 << 18)) return 0;
   const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
   const size_t ml = ((size_t)Hq * T * gm.S1 * 2 * sizeof(float) + 255) / 256 * 256;
   return ml + (size_t)Hkv * gm.HG2 * n_vis * sizeof(float);
@@ -631,9 +630,12 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
   if (!aligned16(q_text) || !aligned16(k)) return fail(SVLM_E_INVALID, "svlm_score: q_text and k must be 16-byte aligned");
   if (q_st % epc || q_sh % epc || k_sh % epc || k_sn % epc || k_sn < D || q_st < 0 || q_sh < 0 || k_sh < 0)
     return fail(SVLM_E_INVALID, "svlm_score: strides must be non-negative multiples of 16 bytes, k_sn >= D");
+  const int out_rows = (agg == SVLM_AGG_QHEAD) ? Hq : (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
   if (dtype == SVLM_F32) {
     // plain fp32 path: row log-sum-exp into the workspace, then the
     // aggregated column means straight into out
+    if (!grid_fits((int64_t)Hq * T, 64) || !grid_fits((n_vis + 255) / 256, 256, out_rows))
+      return fail(SVLM_E_UNSUPPORTED, "svlm_score: %d heads exceed the launch limit", Hq);
     const size_t need = svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis);
     if (!ws || ws_bytes < need)
       return fail(SVLM_E_WORKSPACE, "svlm_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
@@ -658,8 +660,7 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
     f.alpha = alpha;
     f.beta = beta;
     f.out = out;
-    const int rows = (agg == SVLM_AGG_QHEAD) ? Hq : (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
-    launch_score_f32(f, rows, (hipStream_t)stream);
+    launch_score_f32(f, out_rows, (hipStream_t)stream);
     return check_launch("svlm_score");
   }
   // buffer-descriptor ranges and offsets are 32-bit: one head's text queries,
@@ -684,6 +685,9 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
   a.c = scale * kLog2e;
   // pass 1 covers keys [0, q_pos0 + T): everything any text row sees
   const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
+  if (!grid_fits(pass_blocks(Hkv, gm.S1, gm.HG1), 64 * gm.W1) || !grid_fits(pass_blocks(Hkv, gm.S2, gm.HG2), 64 * gm.W2) ||
+      !grid_fits((n_vis + 255) / 256, 256, out_rows))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_score: %d heads exceed the launch limit", Hq);
   a.HG1 = gm.HG1;
   a.HG2 = gm.HG2;
   a.S1 = gm.S1;

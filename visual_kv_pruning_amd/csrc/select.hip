@@ -553,8 +553,10 @@ size_t seg_ws_bytes(int R, const SegPlan& sp, int budget) {
 }  // namespace
 
 extern "C" size_t svlm_select_workspace(int R, int n_vis, int budget, double top_p) {
-  if (R <= 0 || n_vis <= 0 || budget <= 0) return 0;
-  return seg_ws_bytes(R, seg_plan(R, n_vis, budget, top_p), budget);
+  if (R <= 0 || n_vis <= 0 || n_vis > (1 << 18) || budget <= 0 || budget > n_vis) return 0;
+  const SegPlan sp = seg_plan(R, n_vis, budget, top_p);
+  if (!grid_fits((int64_t)R * sp.segs, kThreads)) return 0;
+  return seg_ws_bytes(R, sp, budget);
 }
 
 extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F, int H, int W, double top_p,
@@ -585,6 +587,8 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   a.cand_tok = nullptr;
   hipStream_t st = (hipStream_t)stream;
   const SegPlan sp = seg_plan(R, N, budget, top_p);
+  if (!grid_fits((int64_t)R * sp.segs, kThreads))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_select: %d rows exceed the launch limit", R);
   if (sp.segs > 1 && !tag) {
     const size_t need = seg_ws_bytes(R, sp, budget);
     if (!ws || ws_bytes < need)
@@ -597,7 +601,7 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
     a.C = sp.C;
     SelArgs s1 = a;
     s1.n_stage1 = nullptr;
-    select_rows<false, false, kSegmentPass><<<R * sp.segs, kThreads, 0, st>>>(s1);
+    select_rows<false, false, kSegmentPass><<<(unsigned)((int64_t)R * sp.segs), kThreads, 0, st>>>(s1);
     SelArgs s2 = a;
     s2.scores = a.cand_score;
     s2.row_stride = sp.C;

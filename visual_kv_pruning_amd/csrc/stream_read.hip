@@ -71,7 +71,10 @@ extern "C" int svlm_stream_read(const void* src, int64_t bytes, int workgroups, 
   a.per_wg = (per + 1023) / 1024 * 1024;
   if (a.per_wg > INT32_MAX) return fail(SVLM_E_UNSUPPORTED, "svlm_stream_read: more than 2^31 bytes per workgroup");
   a.sink = sink;
-  const unsigned grid = bytes > 0 ? (unsigned)((bytes + a.per_wg - 1) / a.per_wg) : 1u;
+  const int64_t blocks = bytes > 0 ? (bytes + a.per_wg - 1) / a.per_wg : 1;
+  if (!grid_fits(blocks, 64 * kSrWaves))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_stream_read: %d workgroups exceed the launch limit", workgroups);
+  const unsigned grid = (unsigned)blocks;
   stream_read<<<grid, 64 * kSrWaves, 0, (hipStream_t)stream>>>(a);
   return check_launch("svlm_stream_read");
 }

@@ -18,6 +18,16 @@ int num_cus();                                     // compute units of the curre
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b for non-negative operands, saturated at INT64_MAX
+inline int64_t mul_sat(int64_t a, int64_t b) { return (a != 0 && b > INT64_MAX / a) ? INT64_MAX : a * b; }
+
+// Dispatch limits that every launch here stays within: the x dimension counts
+// work-items (workgroups x threads) below 2^31, y and z count workgroups below
+// 2^16.  Callers form the workgroup counts in 64 bits, before any narrowing.
+inline bool grid_fits(int64_t x_blocks, int threads, int64_t y = 1, int64_t z = 1) {
+  return x_blocks >= 1 && x_blocks <= INT32_MAX / threads && y >= 1 && y < 65536 && z >= 1 && z < 65536;
+}
+
 // ---------------------------------------------------------------------------
 // fp32 operands (SVLM_F32): plain vector-ALU kernels in f32_path.hip
 // ---------------------------------------------------------------------------

@@ -189,6 +189,8 @@ extern "C" int svlm_uvprune_score(const void* v0, const void* vL, int64_t v_sn, 
     return fail(SVLM_E_INVALID, "svlm_uvprune_score: hidden-state pointers must be 16-byte aligned");
   if (!std::isfinite(out_scale) || !std::isfinite(out_offset))
     return fail(SVLM_E_INVALID, "svlm_uvprune_score: out_scale and out_offset must be finite");
+  if (!grid_fits(n_text, kThreads, 2))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_uvprune_score: %d text tokens exceed the launch limit", n_text);
   const size_t need = svlm_uvprune_workspace(n_text, d);
   if (!ws || ws_bytes < need)
     return fail(SVLM_E_WORKSPACE, "svlm_uvprune_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
@@ -211,7 +213,7 @@ extern "C" int svlm_uvprune_score(const void* v0, const void* vL, int64_t v_sn, 
   hipStream_t st = (hipStream_t)stream;
   text_norms<<<dim3((unsigned)n_text, 2), kThreads, 0, st>>>(a);
   text_sums<<<dim3((unsigned)((d + 63) / 64), 2), kThreads, 0, st>>>(a);
-  const int blocks = std::min((n_vis + kThreads / 64 - 1) / (kThreads / 64), 1024);
+  const int blocks = (int)std::min<int64_t>(((int64_t)n_vis + kThreads / 64 - 1) / (kThreads / 64), 1024);
   const size_t lds = (size_t)2 * d * sizeof(float);
   if (lds > 64 * 1024) {
     const hipError_t e =

@@ -365,12 +365,17 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
 
 using namespace svlm;
 
-static int verify_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+static int verify_chunks(int V) { return (int)(((int64_t)V + kChunk - 1) / kChunk); }
+
+// the greedy pass is a (chunks, gamma + 1, batch) grid, the rejection pass (chunks, batch)
+static bool verify_fits(int batch, int gamma, int V) {
+  return grid_fits(verify_chunks(V), kThreads, (int64_t)gamma + 1, batch);
+}
 
 extern "C" size_t svlm_verify_workspace(int batch, int gamma, int V) {
-  if (batch < 1 || gamma < 1 || V < 1) return 0;
+  if (batch < 1 || gamma < 1 || V < 1 || !verify_fits(batch, gamma, V)) return 0;
   const size_t ch = (size_t)verify_chunks(V);
-  const size_t greedy = (size_t)batch * (gamma + 1) * ch * sizeof(ArgMax);
+  const size_t greedy = (size_t)batch * ((size_t)gamma + 1) * ch * sizeof(ArgMax);
   const size_t reject = (size_t)batch * ch * (2 * sizeof(uint64_t) + sizeof(ArgMax)) + (size_t)batch * sizeof(int32_t);
   return (greedy > reject ? greedy : reject) + 256;
 }
@@ -382,6 +387,8 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
     return fail(SVLM_E_INVALID, "svlm_verify: mode must be SVLM_VERIFY_GREEDY or SVLM_VERIFY_REJECT");
   if (batch < 1 || gamma < 1 || V < 1) return fail(SVLM_E_INVALID, "svlm_verify: batch, gamma, V must be >= 1");
   if (!draft_tok || !target || !n_accept || !next_tok) return fail(SVLM_E_INVALID, "svlm_verify: null pointer");
+  if (!verify_fits(batch, gamma, V))
+    return fail(SVLM_E_UNSUPPORTED, "svlm_verify: batch %d and gamma %d must stay below 65536", batch, gamma);
   if (mode == SVLM_VERIFY_REJECT && (!draft_prob || !u))
     return fail(SVLM_E_INVALID, "svlm_verify: rejection mode needs draft_prob and u");
   const size_t need = svlm_verify_workspace(batch, gamma, V);

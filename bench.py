@@ -360,9 +360,10 @@ def main():
             "kernel": "svlm_decode_attn dense verify call (split-K kernel + combine; 25222 keys x 8 KV heads "
                       "x 512 B = 103.3 MB per call)",
             # the same bytes through svlm_stream_read (the attention read pattern and nothing else),
-            # one launch per 103.3 MB in a graph: what a launch of this size gets on this chip
-            "achievable_gbs": achievable["stream_read_per_launch"]["gbs"],
-            "frac_of_achievable": round(verify_gbs / achievable["stream_read_per_launch"]["gbs"], 4),
+            # one launch per 103.3 MB in a graph through the whole cache, on the fastest of five
+            # grids: what a launch of this size gets on this chip
+            "achievable_gbs": achievable["stream_read_per_launch_best"]["gbs"],
+            "frac_of_achievable": round(verify_gbs / achievable["stream_read_per_launch_best"]["gbs"], 4),
         },
         "kernels": kernels,
         "parallel_decoding": {
@@ -408,8 +409,9 @@ def graph_us(torch, fn, calls, reps):
 def measure_achievable(torch, ops, dev, kv, steps):
     """The streaming read of svlm_stream_read: the whole 80-layer K and V cache
     in one launch; 103.3 MB per launch (two adjacent layers of K or of V, the
-    bytes of one dense-verify call) over the verify grid, 80 dependent launches
-    in a graph; and 80 empty launches (the per-launch floor)."""
+    bytes of one dense-verify call), 80 dependent launches in a graph through
+    the whole cache, over the verify grid and over a sweep of grids (the best
+    one is the reference); and 80 empty launches (the per-launch floor)."""
     sink = torch.empty(4096, dtype=torch.float32, device=dev)
     whole = kv.view(-1)
     nb_whole = whole.numel() * whole.element_size()
@@ -417,17 +419,29 @@ def measure_achievable(torch, ops, dev, kv, steps):
     L = kv.shape[1]
     pairs = [kv[w, l:l + 2].reshape(-1) for w in range(2) for l in range(0, L - 1, 2)]
     nb_pair = pairs[0].numel() * pairs[0].element_size()
-    us_pair = graph_us(torch, lambda: [ops.stream_read(t, 216, sink) for t in pairs], len(pairs), steps)
+    sweep = {}
+    for wg in (216, 256, 512, 1024, 2048):
+        us = graph_us(torch, lambda: [ops.stream_read(t, wg, sink) for t in pairs], len(pairs), steps)
+        sweep[f"wg{wg}"] = round(us, 3)
+    us_pair = sweep["wg216"]
+    best_wg = min(sweep, key=sweep.get)
+    us_best = sweep[best_wg]
     us_empty = graph_us(torch, lambda: [ops.stream_read(None, 1, sink) for _ in range(80)], 80, steps)
+
+    def rate(us):
+        return round(nb_pair / (us * 1e-6) / 1e9, 1)
     return {
         "stream_read_whole": {"bytes": nb_whole, "us": round(us_whole, 1),
                               "gbs": round(nb_whole / (us_whole * 1e-6) / 1e9, 1),
                               "what": "one launch over the 80-layer K and V cache, 2048 workgroups"},
-        "stream_read_per_launch": {"bytes": nb_pair, "us_avg": round(us_pair, 3),
-                                   "gbs": round(nb_pair / (us_pair * 1e-6) / 1e9, 1),
-                                   "frac": round(nb_pair / (us_pair * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                   "what": "103.3 MB (one dense-verify call's bytes) per launch over 216 "
-                                           "workgroups, 80 dependent launches in a graph"},
+        "stream_read_per_launch": {"bytes": nb_pair, "us_avg": round(us_pair, 3), "gbs": rate(us_pair),
+                                   "frac": round(rate(us_pair) / HBM_PEAK_GBS, 4),
+                                   "what": "103.3 MB (one dense-verify call's bytes) per launch over the verify "
+                                           "grid (216 workgroups), 80 dependent launches in a graph"},
+        "stream_read_per_launch_best": {"bytes": nb_pair, "us_avg": us_best, "gbs": rate(us_best),
+                                        "frac": round(rate(us_best) / HBM_PEAK_GBS, 4), "grid": best_wg,
+                                        "us_by_grid": sweep,
+                                        "what": "the same 80 launches over 216 to 2048 workgroups; the fastest"},
         "empty_launch_us": round(us_empty, 3),
         "what": "svlm_stream_read: the attention kernels' read pattern (1 KB LDS-DMA transfers, 16 KB in "
                 "flight per wave) and nothing else",

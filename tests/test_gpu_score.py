@@ -119,6 +119,25 @@ def test_wide_score_range():
     _compare(_gpu_score(p, cfg, "kvhead"), _ref(p, cfg, "kvhead"), "C2 q x4")
 
 
+def test_late_logit_spikes():
+    """Keys set to 8, 16 and 32 times one text query (exact in bf16), placed
+    past the first tile of their key splits: that query's scores with them
+    lie ~130 to ~520 log2 units above everything before them, so pass 1's
+    per-lane reference must be raised long after the first keys set it (the
+    unchecked tile form overflows its limit there and the tile is redone with
+    rescaling).  Other rows of the group see spikes of either sign."""
+    cfg = W.C2
+    p = W.prefill_layer(cfg, 0)
+    k = p.k.copy()
+    for pos, beta, t0, h0 in ((192 * 10 + 100, 8.0, 3, 0), (192 * 25 + 130, 16.0, 3, 0),
+                              (192 * 40 + 170, 32.0, 17, 2), (cfg.n_vis - 40, 8.0, 40, 5)):
+        k[h0 // cfg.group, pos, :] = beta * p.q_text[t0, h0, :]
+    p = dataclasses.replace(p, k=k)
+    log("score case late logit spikes")
+    for agg in ("qhead", "kvhead"):
+        _compare(_gpu_score(p, cfg, agg), _ref(p, cfg, agg), f"C2 late spikes {agg}")
+
+
 @dataclasses.dataclass
 class _Layer:
     q_text: np.ndarray

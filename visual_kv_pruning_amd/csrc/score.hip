@@ -32,7 +32,7 @@ namespace {
 constexpr float kNegInf = -INFINITY;
 constexpr int kTileKeys = 64;      // keys per staged K tile
 constexpr float kRescaleSum = 256.f;  // a lane's 4-key weight sum above this raises its reference maximum
-constexpr int kLseBatch = 16;      // pass-1 partials loaded at once when a row's log-sum-exp is formed
+constexpr int kLseBatch = 32;      // pass-1 partials per row loaded at once when a row's log-sum-exp is formed
 
 struct ScoreArgs {
   const uint16_t* q;
@@ -43,7 +43,8 @@ struct ScoreArgs {
   int HG1, HG2;  // head groups (workgroups) per KV head, pass 1 and pass 2
   float c;  // scale * log2(e), > 0
   int S1, kps1, S2, kps2;
-  float* ml;   // [Hq][T][S1][2]: per split, (reference maximum in raw-score units, sum)
+  float* ml;   // [Hq][S1][T][2]: per split, (reference maximum in raw-score units, sum); split-major,
+               // so one split's rows are contiguous for the loads that merge them
   float* grp;  // [Hkv * HG][n_vis]: per head group, the sum over its heads of the column means
   int agg;
   float alpha, beta;
@@ -76,13 +77,24 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2,
 }
 
 // Ring depth of the shared K tiles: a wave issues PW transfers per tile and
-// at most NS - 1 tiles are outstanding (6-bit wait counter); LDS holds NS tiles.
-template <int D, int W>
+// at most NS - 1 tiles are outstanding (6-bit wait counter); LDS holds NS
+// tiles, at most MAXNS.  A tile's arithmetic takes several microseconds, far
+// longer than staging one, so a shallow ring keeps the key loop fed; deeper
+// rings only add to the burst of loads every workgroup issues at once when
+// the kernel starts.  Measured per 72B-shape layer: pass 1 best at 4 slots,
+// pass 2 at 3.
+#ifndef SVLM_SCORE_RING1
+#define SVLM_SCORE_RING1 4
+#endif
+#ifndef SVLM_SCORE_RING2
+#define SVLM_SCORE_RING2 3
+#endif
+template <int D, int W, int MAXNS>
 constexpr int score_ring_depth() {
   constexpr int TB = kTileKeys * D * 2;
   constexpr int PW = (TB / 1024) / W;
   int ns = 2;
-  while (ns < 8 && ns * PW <= 63 && (size_t)(ns + 1) * TB <= 128 * 1024) ++ns;
+  while (ns < MAXNS && ns * PW <= 63 && (size_t)(ns + 1) * TB <= 128 * 1024) ++ns;
   return ns;
 }
 
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
     }
     const int tq = rb * 16 + c;
     if (g4 == 0 && hl < a.G && tq < a.T)
-      *(float2*)(a.ml + (((int64_t)h * a.T + tq) * a.S1 + s) * 2) = make_float2(m, ll);
+      *(float2*)(a.ml + (((int64_t)h * a.S1 + s) * a.T + tq) * 2) = make_float2(m, ll);
   }
 }
 
@@ -393,31 +405,57 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
   Ring kr;
   kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)v_begin * a.k_sn, max(v_end - v_begin, 0), a.k_sn, ring, wave);
 
+  // Row log-sum-exp (log2 units of the scaled score) from the pass-1
+  // partials, in split order; padded rows get +inf and so contribute
+  // exp2(-inf) = 0.  Lane = row, so each load reads consecutive rows of one
+  // split (the partials are split-major).  The first kLseBatch partials of
+  // the lane's rows are loaded before anything else, so their round trip
+  // waits behind no other load (memory operations complete in issue order);
+  // the K tiles are staged behind them, and the queries are loaded once the
+  // partials are merged, when their registers are free.
+  constexpr int RPL = (RB * 16 + 63) / 64;  // rows per lane
+  float M[RPL], L[RPL];
+  auto load_parts = [&](int s0, float2 (&part)[RPL][kLseBatch]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int tq = lane + 64 * r;
+      const float2* p = (const float2*)(a.ml + ((int64_t)h * a.S1 * a.T + min(tq, a.T - 1)) * 2);
+#pragma unroll
+      for (int j = 0; j < kLseBatch; ++j)
+        part[r][j] = (tq < a.T && s0 + j < a.S1) ? p[(int64_t)(s0 + j) * a.T] : make_float2(kNegInf, 0.f);
+    }
+  };
+  auto merge_parts = [&](const float2 (&part)[RPL][kLseBatch]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int j = 0; j < kLseBatch; ++j) merge_ml(M[r], L[r], part[r][j].x, part[r][j].y, a.c);
+  };
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    M[r] = kNegInf;
+    L[r] = 0.f;
+  }
+  {
+    float2 part[RPL][kLseBatch];
+    load_parts(0, part);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
+    merge_parts(part);
+  }
+  for (int s0 = kLseBatch; s0 < a.S1; s0 += kLseBatch) {
+    float2 part[RPL][kLseBatch];
+    load_parts(s0, part);
+    merge_parts(part);
+  }
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int tq = lane + 64 * r;
+    if (tq < RB * 16) sm_lse[wave][tq] = (tq < a.T && L[r] > 0.f) ? M[r] * a.c + log2f(L[r]) : INFINITY;
+  }
+
   u32x4 qreg[RB][KK];
   load_q<D, RB>(a, h, qreg);
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
-
-  // row log-sum-exp (log2 units of the scaled score) from the pass-1 partials,
-  // in split order; padded rows get +inf and so contribute exp2(-inf) = 0
-  // (the partials are loaded kLseBatch splits at a time, so a row costs
-  // ceil(S1 / kLseBatch) memory round trips rather than S1)
-  for (int tq = lane; tq < RB * 16; tq += 64) {
-    float v = INFINITY;
-    if (tq < a.T) {
-      const float2* p = (const float2*)(a.ml + ((int64_t)h * a.T + tq) * a.S1 * 2);
-      float M = kNegInf, L = 0.f;
-      for (int s0 = 0; s0 < a.S1; s0 += kLseBatch) {
-        float2 part[kLseBatch];
-#pragma unroll
-        for (int j = 0; j < kLseBatch; ++j) part[j] = (s0 + j < a.S1) ? p[s0 + j] : make_float2(kNegInf, 0.f);
-#pragma unroll
-        for (int j = 0; j < kLseBatch; ++j) merge_ml(M, L, part[j].x, part[j].y, a.c);
-      }
-      v = (L > 0.f) ? M * a.c + log2f(L) : INFINITY;
-    }
-    sm_lse[wave][tq] = v;
-  }
   wait_lgkmcnt0();
   float lse[RB][4];  // rows 16 rb + 4 g4 + i
 #pragma unroll
@@ -455,7 +493,8 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
     if (key < v_end) emit(direct ? g : g * a.HG2 + hg, key, v * grp_scale);
   };
 
-  wait_vmcnt<(NS - 1) * Ring::PW>();  // the query loads, issued first, have landed
+  // (the compiler waits for the query loads before their first use; tile t's
+  // wait below also covers the loads issued after it)
   for (int t = 0; t < n_tiles; ++t) {
     wait_vmcnt<(NS - 2) * Ring::PW>();
     wait_lgkmcnt0();  // this wave's column means of tile t-1 are in LDS
@@ -519,11 +558,11 @@ inline int64_t pass_blocks(int Hkv, int S, int HG) { return ((int64_t)Hkv * S + 
 
 template <int D, int RB, int W>
 void launch_pass1(const ScoreArgs& a, hipStream_t st) {
-  score_pass1<D, RB, W, score_ring_depth<D, W>()><<<(unsigned)pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
+  score_pass1<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING1>()><<<(unsigned)pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
 }
 template <int D, int RB, int W>
 void launch_pass2(const ScoreArgs& a, hipStream_t st) {
-  score_pass2<D, RB, W, score_ring_depth<D, W>()><<<(unsigned)pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
+  score_pass2<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING2>()><<<(unsigned)pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
 }
 
 template <int D, int RB>

@@ -425,11 +425,23 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
         part[r][j] = (tq < a.T && s0 + j < a.S1) ? p[(int64_t)(s0 + j) * a.T] : make_float2(kNegInf, 0.f);
     }
   };
+  // a batch of partials joins the running (M, L) in two steps: the largest
+  // reference first, then every sum weighed against it (one exp2 per
+  // partial, no branches; a split that saw no key has (-inf, 0) and adds 0)
   auto merge_parts = [&](const float2 (&part)[RPL][kLseBatch]) {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r)
+    for (int r = 0; r < RPL; ++r) {
+      float bm = kNegInf;
 #pragma unroll
-      for (int j = 0; j < kLseBatch; ++j) merge_ml(M[r], L[r], part[r][j].x, part[r][j].y, a.c);
+      for (int j = 0; j < kLseBatch; ++j) bm = fmaxf(bm, part[r][j].x);
+      const float m_new = fmaxf(M[r], bm);
+      const float mref = (m_new == kNegInf) ? 0.f : m_new;
+      float acc = (M[r] == kNegInf) ? 0.f : L[r] * fast_exp2((M[r] - mref) * a.c);
+#pragma unroll
+      for (int j = 0; j < kLseBatch; ++j) acc = fmaf(part[r][j].y, fast_exp2((part[r][j].x - mref) * a.c), acc);
+      M[r] = m_new;
+      L[r] = acc;
+    }
   };
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {

@@ -145,48 +145,6 @@ struct KRing {
   static __device__ unsigned koff(int r, int kk, int g4) { return r * ROWB + (((kk * 4 + g4) ^ (r % CH)) * 16); }
 };
 
-// the KK K-operand chunks of one 16-key block of a staged tile
-template <int KK>
-__device__ __forceinline__ void read_k_block(unsigned base, const unsigned (&ko)[KK], u32x4 (&kq)[KK]) {
-  unsigned ad[KK];
-#pragma unroll
-  for (int e = 0; e < KK; ++e) ad[e] = base + ko[e];
-  if constexpr (KK == 4) lds_read_b128x4(kq, ad);
-  else lds_read_b128x2(kq, ad);
-}
-
-// S = Q K^T for two 16-key blocks and every text row block (lane: rows
-// 16 rb + 4 g4 + i, key c of each block)
-template <int RB, int KK>
-__device__ __forceinline__ void qk_half(const u32x4 (&q)[RB][KK], const u32x4 (&kq)[2][KK], f32x4 (&S)[RB][2]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s0 = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[0][kk]), s0);
-      s1 = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[1][kk]), s1);
-    }
-    S[rb][0] = s0;
-    S[rb][1] = s1;
-  }
-}
-
-// the lane's part of the column sums of P = exp2(c s - lse) for the two key blocks
-template <int RB>
-__device__ __forceinline__ void colsum_half(const f32x4 (&S)[RB][2], const float (&lse)[RB][4], float c, float& c0,
-                                            float& c1) {
-  c0 = 0.f;
-  c1 = 0.f;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c0 += fast_exp2(fmaf(S[rb][0][i], c, -lse[rb][i]));
-      c1 += fast_exp2(fmaf(S[rb][1][i], c, -lse[rb][i]));
-    }
-}
-
 // the lane's part of the column sum of P = exp2(c s - lse) for one 16-key
 // block (lane: rows 16 rb + 4 g4 + i, key c).  One block at a time keeps the
 // score accumulators few enough to live in ordinary VGPRs next to the query
@@ -306,10 +264,11 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
     wg_barrier();                       // every share of tile t has landed; tile t-1 is retired
     kr.stage((t + NS - 1) % NS, t + NS - 1);
     const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
+    u32x4 kq2[2][KK];  // K operands of two blocks per LDS wait
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {  // one 16-key block at a time keeps the live registers low
-      u32x4 kq[KK];
-      read_k_block<KK>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq);
+    for (int kb = 0; kb < 4; ++kb) {  // one 16-key block of products at a time keeps the live registers low
+      if (kb % 2 == 0) read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq2);
+      const u32x4 (&kq)[KK] = kq2[kb % 2];
       const int key0 = k_begin + t * kTileKeys + 16 * kb;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -516,10 +475,11 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
     const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
     float col[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4 kq[KK];
-      read_k_block<KK>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq);
-      col[kb] = qk_colsum_block<RB, KK>(qreg, kq, lse, a.c);
+    for (int kp = 0; kp < 2; ++kp) {  // K operands of two blocks per LDS wait
+      u32x4 kq2[2][KK];
+      read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(kp * 32 * Ring::ROWB), ko, kq2);
+      col[2 * kp] = qk_colsum_block<RB, KK>(qreg, kq2[0], lse, a.c);
+      col[2 * kp + 1] = qk_colsum_block<RB, KK>(qreg, kq2[1], lse, a.c);
     }
     // column sums over the rows held by the four lane groups; lane (c, g4) then
     // keeps key 16 g4 + c of the tile

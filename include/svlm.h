@@ -343,6 +343,35 @@ int svlm_verify(int mode, int batch, int gamma, int V, const int32_t* draft_tok,
  * ------------------------------------------------------------------------ */
 int svlm_stream_read(const void* src, int64_t bytes, int workgroups, float* sink, void* stream);
 
+/* ------------------------------------------------------------------------
+ * svlm_debug_flags - device preconditions violated since the last call.
+ * For callers debugging their inputs: a library built with -DSVLM_DEBUG
+ * (libsvlm_debug.so beside libsvlm.so) checks, inside the kernels, the
+ * device-side preconditions stated per call above and, beside the clamping
+ * every build does, sets one bit per kind of violation:
+ *   SVLM_DBG_KV_LEN       an attention length (kv_len, or an index list's
+ *                         length) outside [nq, max_kv_len]
+ *   SVLM_DBG_KV_INDEX     an attention index-list entry outside [0, kv_rows)
+ *   SVLM_DBG_GATHER_INDEX a gather index outside [0, n_src)
+ *   SVLM_DBG_DRAFT_TOKEN  a draft token outside [0, V)
+ *   SVLM_DBG_PROB_RANGE   a target or draft probability read by the
+ *                         rejection test outside [0, 1] (or NaN)
+ *   SVLM_DBG_SCORE_RANGE  a selection score outside [0, 1] (or NaN)
+ * *flags receives the bits set since the previous call, which clears them.
+ * Call it when the work to inspect has completed (the copy of the flags
+ * synchronises with the default stream only).  Without SVLM_DEBUG it stores
+ * 0 and returns SVLM_E_UNSUPPORTED; it launches nothing either way.
+ * ------------------------------------------------------------------------ */
+enum svlm_debug_flag {
+  SVLM_DBG_KV_LEN = 1u,
+  SVLM_DBG_KV_INDEX = 2u,
+  SVLM_DBG_GATHER_INDEX = 4u,
+  SVLM_DBG_DRAFT_TOKEN = 8u,
+  SVLM_DBG_PROB_RANGE = 16u,
+  SVLM_DBG_SCORE_RANGE = 32u
+};
+int svlm_debug_flags(unsigned* flags);
+
 #ifdef __cplusplus
 }
 #endif

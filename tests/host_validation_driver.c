@@ -139,6 +139,14 @@ int main(void) {
          "verify gamma");
   expect(svlm_stream_read(f, (int64_t)1 << 40, INT32_MAX, ff, 0), SVLM_E_UNSUPPORTED, "stream grid");
 
+  /* debug flags: only a library built with SVLM_DEBUG keeps them */
+  {
+    unsigned fl = 7;
+    expect(svlm_debug_flags(&fl), SVLM_E_UNSUPPORTED, "debug flags");
+    if (fl != 0) ++fails;
+    expect(svlm_debug_flags(0), SVLM_E_INVALID, "debug flags null");
+  }
+
   (void)big;
   if (fails) fprintf(stderr, "%d unexpected statuses\n", fails);
   return fails;

@@ -202,3 +202,32 @@ def test_noalloc_refuses_state_beyond_its_scratch_on_the_host(lib):
                                       L.SVLM_BF16, 1, 64, 64, 8, 128, C.c_float(0.1), 1, fake, fake, 256, None)
     assert st == L.SVLM_E_UNSUPPORTED
     assert b"scratch" in lib.svlm_last_error()
+
+
+def test_debug_library_exports_every_symbol():
+    """libsvlm_debug.so (SVLM_DEBUG: kernels record violated device
+    preconditions) carries the same ABI."""
+    if not os.path.exists(L.DEBUG_LIB_PATH):
+        pytest.fail("libsvlm_debug.so is not built (run python -m visual_kv_pruning_amd.build)")
+    dbg = L.load_debug()
+    assert dbg.svlm_abi_version() == L.ABI_VERSION
+    for name in declared_symbols():
+        assert hasattr(dbg, name), name
+
+
+def test_debug_flags_outside_a_debug_build(lib):
+    v = C.c_uint(7)
+    assert lib.svlm_debug_flags(C.byref(v)) == L.SVLM_E_UNSUPPORTED and v.value == 0
+    assert b"SVLM_DEBUG" in lib.svlm_last_error()
+    assert lib.svlm_debug_flags(None) == L.SVLM_E_INVALID
+
+
+def test_debug_flags_of_the_debug_build_without_work():
+    """Reading the flags launches nothing: OK (flags 0) where a device is
+    present, SVLM_E_HIP where none is."""
+    dbg = L.load_debug()
+    v = C.c_uint(7)
+    st = dbg.svlm_debug_flags(C.byref(v))
+    assert st in (L.SVLM_OK, L.SVLM_E_HIP)
+    assert v.value == 0 or st == L.SVLM_OK
+    assert dbg.svlm_debug_flags(None) == L.SVLM_E_INVALID

@@ -55,3 +55,23 @@ extern "C" const char* svlm_status_string(int status) {
 }
 
 extern "C" const char* svlm_last_error(void) { return svlm::g_last_error; }
+
+extern "C" int svlm_debug_flags(unsigned* flags) {
+  if (!flags) return svlm::fail(SVLM_E_INVALID, "svlm_debug_flags: null pointer");
+  *flags = 0;
+#ifdef SVLM_DEBUG
+  using namespace svlm;
+  bool (*const take[])(unsigned*) = {debug_take_decode_attn, debug_take_f32_path, debug_take_gather,
+                                     debug_take_select, debug_take_verify};
+  unsigned all = 0;
+  for (auto t : take) {
+    unsigned v = 0;
+    if (!t(&v)) return fail(SVLM_E_HIP, "svlm_debug_flags: reading the device flags failed");
+    all |= v;
+  }
+  *flags = all;
+  return SVLM_OK;
+#else
+  return svlm::fail(SVLM_E_UNSUPPORTED, "svlm_debug_flags: this library was built without SVLM_DEBUG");
+#endif
+}

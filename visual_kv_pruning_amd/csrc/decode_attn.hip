@@ -142,7 +142,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
   const int b = ph / a.Hkv;
   const int row_base = blockIdx.y * RP;
 
-  const int n_kv = min(max(a.kv_len[(int64_t)b * a.len_sb + (int64_t)h * a.len_sh], 0), a.max_kv_len);
+  const int n_raw = a.kv_len[(int64_t)b * a.len_sb + (int64_t)h * a.len_sh];
+  if (threadIdx.x == 0) debug_check(n_raw >= a.nq && n_raw <= a.max_kv_len, SVLM_DBG_KV_LEN);
+  const int n_kv = min(max(n_raw, 0), a.max_kv_len);
   const int k_begin = s * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, n_kv);
   // this wave's blocks: keys k_begin + 64 j + 16 wave, j < n_my
@@ -184,6 +186,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
       int r = -1;
       if (k_begin + p < k_end) {
         r = idx[k_begin + p];
+        debug_check(r >= 0 && r < a.kv_rows, SVLM_DBG_KV_INDEX);
         if (r < 0 || r >= a.kv_rows) r = -1;
       }
       sm_idx[p] = r;
@@ -976,3 +979,7 @@ extern "C" int svlm_decode_attn_noalloc(const void* q, int64_t q_sb, const void*
                           1, 0, max_kv_len, dtype, batch, nq, Hq, Hkv, D, scale, causal_tail, out, lse, num_splits,
                           ws, need > 0 ? kScratchBytes : 0, stream);
 }
+
+#ifdef SVLM_DEBUG
+bool svlm::debug_take_decode_attn(unsigned* out) { return debug_take_here(out); }
+#endif

@@ -46,7 +46,9 @@ __global__ __launch_bounds__(64) void attn_f32_rows(AttnF32Args a) {
   const int i = (row / a.Hq) % a.nq;
   const int b = row / (a.Hq * a.nq);
   const int g = h / (a.Hq / a.Hkv);
-  const int n_kv = min(max(a.kv_len[(int64_t)b * a.len_sb + (int64_t)g * a.len_sh], 0), a.max_kv_len);
+  const int n_raw = a.kv_len[(int64_t)b * a.len_sb + (int64_t)g * a.len_sh];
+  if (threadIdx.x == 0) debug_check(n_raw >= a.nq && n_raw <= a.max_kv_len, SVLM_DBG_KV_LEN);
+  const int n_kv = min(max(n_raw, 0), a.max_kv_len);
   const int lim = a.causal ? n_kv - a.nq + i + 1 : n_kv;
   const float* qrow = a.q + (int64_t)b * a.q_sb + ((int64_t)i * a.Hq + h) * D;
 #pragma unroll
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(64) void attn_f32_rows(AttnF32Args a) {
   auto key_row = [&](int p) -> int {
     if (!idx) return p;
     const int r = idx[p];
+    debug_check(r >= 0 && r < a.kv_rows, SVLM_DBG_KV_INDEX);
     return (r >= 0 && r < a.kv_rows) ? r : -1;
   };
   float m = -INFINITY, l = 0.f;
@@ -177,3 +180,7 @@ void launch_score_f32(const ScoreF32Args& a, int rows, hipStream_t st) {
 }
 
 }  // namespace svlm
+
+#ifdef SVLM_DEBUG
+bool svlm::debug_take_f32_path(unsigned* out) { return debug_take_here(out); }
+#endif

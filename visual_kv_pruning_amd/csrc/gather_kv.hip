@@ -33,8 +33,12 @@ __global__ __launch_bounds__(256) void gather_rows(GatherArgs a) {
   const int which = blockIdx.z;        // 0: K, 1: V
   if (j >= a.n_idx + a.n_tail) return;
   int srow;
-  if (j < a.n_idx) srow = a.idx[(int64_t)g * a.idx_sh + j];
-  else srow = a.tail_start + (j - a.n_idx);
+  if (j < a.n_idx) {
+    srow = a.idx[(int64_t)g * a.idx_sh + j];
+    if (ch == 0 && which == 0) debug_check(srow >= 0 && srow < a.n_src, SVLM_DBG_GATHER_INDEX);
+  } else {
+    srow = a.tail_start + (j - a.n_idx);
+  }
   u32x4 val = {0u, 0u, 0u, 0u};
   if (srow >= 0 && srow < a.n_src)
     val = *(const u32x4*)(a.src[which] + ((int64_t)g * a.s_sh + (int64_t)srow * a.s_sn) * ES + ch * 16);
@@ -96,3 +100,7 @@ extern "C" int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh
   }
   return check_launch("svlm_gather_kv");
 }
+
+#ifdef SVLM_DEBUG
+bool svlm::debug_take_gather(unsigned* out) { return debug_take_here(out); }
+#endif

@@ -62,6 +62,7 @@ struct SelArgs {
 enum : int { kPlain = 0, kSegmentPass = 1, kCandidatePass = 2 };
 
 __device__ __forceinline__ unsigned key_of(float s) {
+  debug_check(s >= 0.f && s <= 1.f, SVLM_DBG_SCORE_RANGE);
   unsigned k = f_bits(s);
   return (k == 0x80000000u) ? 0u : k;       // -0 orders as +0
 }
@@ -621,3 +622,7 @@ extern "C" int svlm_select(const float* scores, int64_t row_stride, int R, int F
   }
   return check_launch("svlm_select");
 }
+
+#ifdef SVLM_DEBUG
+bool svlm::debug_take_select(unsigned* out) { return debug_take_here(out); }
+#endif

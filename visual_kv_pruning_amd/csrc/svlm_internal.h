@@ -29,6 +29,35 @@ inline bool grid_fits(int64_t x_blocks, int threads, int64_t y = 1, int64_t z = 
 }
 
 // ---------------------------------------------------------------------------
+// debug builds (-DSVLM_DEBUG): kernels record violated device preconditions.
+// Device variables are not shared between the library's code objects, so
+// each source file holds its own flag word and a host function that takes
+// (reads and clears) it; svlm_debug_flags() collects them.
+// ---------------------------------------------------------------------------
+#ifdef SVLM_DEBUG
+static __device__ unsigned g_debug_flags;
+__device__ __forceinline__ void debug_check(bool ok, unsigned bit) {
+  if (!ok) __hip_atomic_fetch_or(&g_debug_flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this file's flags, cleared; false on a HIP error
+static inline bool debug_take_here(unsigned* out) {
+  unsigned v = 0;
+  const unsigned zero = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof v) != hipSuccess) return false;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof zero) != hipSuccess) return false;
+  *out = v;
+  return true;
+}
+bool debug_take_decode_attn(unsigned* out);
+bool debug_take_f32_path(unsigned* out);
+bool debug_take_gather(unsigned* out);
+bool debug_take_select(unsigned* out);
+bool debug_take_verify(unsigned* out);
+#else
+__device__ __forceinline__ void debug_check(bool, unsigned) {}
+#endif
+
+// ---------------------------------------------------------------------------
 // fp32 operands (SVLM_F32): plain vector-ALU kernels in f32_path.hip
 // ---------------------------------------------------------------------------
 struct AttnF32Args {

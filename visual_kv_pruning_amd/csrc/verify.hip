@@ -72,7 +72,10 @@ struct VerifyArgs {
   int32_t* r_first;     // reject: [B] first rejected position (written by chunk 0)
 };
 
-__device__ __forceinline__ int clamp_tok(int t, int V) { return min(max(t, 0), V - 1); }
+__device__ __forceinline__ int clamp_tok(int t, int V) {
+  debug_check(t >= 0 && t < V, SVLM_DBG_DRAFT_TOKEN);
+  return min(max(t, 0), V - 1);
+}
 
 // first rejected position (gamma if all accepted); identical in every
 // workgroup.  Called by one whole wave: lane i tests position i0 + i, all
@@ -89,6 +92,7 @@ __device__ int first_reject_wave(const VerifyArgs& a, int b) {
       const double pd = a.target[((int64_t)b * (G + 1) + i) * a.V + d];
       const double qd = a.q[((int64_t)b * G + i) * a.V + d];
       const double ui = a.u[(int64_t)b * (G + 1) + i];
+      debug_check(pd >= 0.0 && pd <= 1.0 && qd >= 0.0 && qd <= 1.0, SVLM_DBG_PROB_RANGE);
       rej = !(ui * qd <= pd);
     }
     const unsigned long long m = __builtin_amdgcn_ballot_w64(rej);
@@ -146,6 +150,10 @@ __global__ __launch_bounds__(kThreads) void greedy_final(VerifyArgs a) {
       for (int r = 0; r < rows; ++r) {
         const int i = i0 + r;
         const int am = s_am[r];
+        if (i < a.gamma) {
+          const int d = a.draft[(int64_t)b * a.gamma + i];
+          debug_check(d >= 0 && d < a.V, SVLM_DBG_DRAFT_TOKEN);
+        }
         if (i == a.gamma || a.draft[(int64_t)b * a.gamma + i] != am) {
           a.n_accept[b] = i;
           a.next_tok[b] = am;
@@ -420,3 +428,7 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
   }
   return check_launch("svlm_verify");
 }
+
+#ifdef SVLM_DEBUG
+bool svlm::debug_take_verify(unsigned* out) { return debug_take_here(out); }
+#endif

@@ -21,7 +21,10 @@ struct GatherArgs {
   int n_idx, tail_start, n_tail;
 };
 
-// ES: bytes per element; strides are in elements
+// ES: bytes per element; strides are in elements.  A thread moves one
+// 16-byte chunk of one row from K and from V, both loads issued before either
+// store.  (Measured per 72B-shape layer: 5.6 us against 6.0 with one tensor
+// per thread; two or four rows per thread were slower.)
 template <int D, int ES>
 __global__ __launch_bounds__(256) void gather_rows(GatherArgs a) {
   constexpr int CH = D * ES / 16;      // 16-byte chunks per row
@@ -30,19 +33,23 @@ __global__ __launch_bounds__(256) void gather_rows(GatherArgs a) {
   const int j = blockIdx.x * RPB + t / CH;
   const int ch = t % CH;
   const int g = blockIdx.y;
-  const int which = blockIdx.z;        // 0: K, 1: V
   if (j >= a.n_idx + a.n_tail) return;
   int srow;
   if (j < a.n_idx) {
     srow = a.idx[(int64_t)g * a.idx_sh + j];
-    if (ch == 0 && which == 0) debug_check(srow >= 0 && srow < a.n_src, SVLM_DBG_GATHER_INDEX);
+    if (ch == 0) debug_check(srow >= 0 && srow < a.n_src, SVLM_DBG_GATHER_INDEX);
   } else {
     srow = a.tail_start + (j - a.n_idx);
   }
-  u32x4 val = {0u, 0u, 0u, 0u};
-  if (srow >= 0 && srow < a.n_src)
-    val = *(const u32x4*)(a.src[which] + ((int64_t)g * a.s_sh + (int64_t)srow * a.s_sn) * ES + ch * 16);
-  *(u32x4*)(a.dst[which] + ((int64_t)g * a.d_sh + (int64_t)j * a.d_sn) * ES + ch * 16) = val;
+  u32x4 val[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (srow >= 0 && srow < a.n_src) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv)
+      val[kv] = *(const u32x4*)(a.src[kv] + ((int64_t)g * a.s_sh + (int64_t)srow * a.s_sn) * ES + ch * 16);
+  }
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv)
+    *(u32x4*)(a.dst[kv] + ((int64_t)g * a.d_sh + (int64_t)j * a.d_sn) * ES + ch * 16) = val[kv];
 }
 
 }  // namespace
@@ -86,10 +93,10 @@ extern "C" int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh
   a.n_idx = n_idx;
   a.tail_start = tail_start;
   a.n_tail = n_tail;
-  const int rpb = 256 / (D / epc);
-  if (!grid_fits((n + rpb - 1) / rpb, 256, Hkv, 2))
+  const int rpb = 256 / (D / epc);  // rows per block
+  if (!grid_fits((n + rpb - 1) / rpb, 256, Hkv))
     return fail(SVLM_E_UNSUPPORTED, "svlm_gather_kv: %d rows x %d KV heads exceed the launch limit", n, Hkv);
-  dim3 grid((unsigned)((n + rpb - 1) / rpb), (unsigned)Hkv, 2);
+  dim3 grid((unsigned)((n + rpb - 1) / rpb), (unsigned)Hkv);
   hipStream_t st = (hipStream_t)stream;
   if (dtype == SVLM_F32) {
     if (D == 128) gather_rows<128, 4><<<grid, 256, 0, st>>>(a);

@@ -14,7 +14,8 @@
 // Three launches: text row norms (one workgroup per text row and layer), the
 // normalised text sums (64 dimensions per workgroup, rows split over its four
 // waves and added in a fixed order), and
-// the video rows (one wave per row, the two text sums staged in LDS).  All
+// the video rows (one wave per row, the two text sums staged in LDS, the
+// rows read with nontemporal loads since each byte is read once).  All
 // reductions run in a fixed order, so results are deterministic.  A zero
 // vector's similarities are 0.
 #include <algorithm>
@@ -146,14 +147,16 @@ __global__ __launch_bounds__(kThreads) void video_scores(UvArgs a) {
     for (int c0 = 0; c0 < full; c0 += 64 * kRowUnroll) {
       u32x4 w0[kRowUnroll], wL[kRowUnroll];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {  // every load of the group first
-        w0[u] = r0[c0 + 64 * u + lane];
-        wL[u] = rL[c0 + 64 * u + lane];
+      for (int u = 0; u < kRowUnroll; ++u) {  // every load of the group first; nontemporal: read once
+        w0[u] = __builtin_nontemporal_load(&r0[c0 + 64 * u + lane]);
+        wL[u] = __builtin_nontemporal_load(&rL[c0 + 64 * u + lane]);
       }
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) row_chunk(w0[u], wL[u], sm_xbar, d4, c0 + 64 * u + lane, ss0, dt0, ssL, dtL);
     }
-    for (int c = full + lane; c < chunks; c += 64) row_chunk(r0[c], rL[c], sm_xbar, d4, c, ss0, dt0, ssL, dtL);
+    for (int c = full + lane; c < chunks; c += 64)
+      row_chunk(__builtin_nontemporal_load(&r0[c]), __builtin_nontemporal_load(&rL[c]), sm_xbar, d4, c, ss0, dt0,
+                ssL, dtL);
     ss0 = wave_sum(ss0);
     dt0 = wave_sum(dt0);
     ssL = wave_sum(ssL);

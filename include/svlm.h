@@ -199,8 +199,10 @@ int svlm_gather_kv(const void* k_src, const void* v_src, int64_t s_sh, int64_t s
  *         max_kv_len (values are clamped into [0, max_kv_len]).
  * out: [B][nq][Hq][D] fp32 contiguous; lse: [B][nq][Hq] fp32 or NULL.
  * num_splits: key-range splits per (batch, KV head); 0 picks one for the
- *   chip.  With more than one split the partial (max, sum, output) states go
- *   to ws and are merged in a fixed order.
+ *   chip, or takes SVLM_NUM_SPLITS from the environment when that holds a
+ *   positive integer (read once per process; the *_workspace() queries use
+ *   the same rule).  With more than one split the partial (max, sum, output)
+ *   states go to ws and are merged in a fixed order.
  * ws: svlm_decode_attn_workspace(batch, nq, Hq, Hkv, D, max_kv_len, num_splits)
  *   bytes (0 when one split suffices); no initial contents are needed.  Two
  *   calls that overlap in time must not share a workspace.  SVLM_F32 uses no

@@ -231,3 +231,33 @@ def test_debug_flags_of_the_debug_build_without_work():
     assert st in (L.SVLM_OK, L.SVLM_E_HIP)
     assert v.value == 0 or st == L.SVLM_OK
     assert dbg.svlm_debug_flags(None) == L.SVLM_E_INVALID
+
+
+def _workspace_in_subprocess(env_value):
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from visual_kv_pruning_amd import _lib as L; lib = L.load(); "
+            "print(lib.svlm_decode_attn_workspace(1, 6, 64, 8, 128, 25222, 0), "
+            "lib.svlm_decode_attn_workspace(1, 6, 64, 8, 128, 25222, 5), "
+            "lib.svlm_decode_attn_indexed_workspace(1, 1, 64, 8, 128, 2638, 0), "
+            "lib.svlm_decode_attn_indexed_workspace(1, 1, 64, 8, 128, 2638, 5))")
+    env = dict(os.environ)
+    env.pop("SVLM_NUM_SPLITS", None)
+    if env_value is not None:
+        env["SVLM_NUM_SPLITS"] = env_value
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, cwd=root, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return [int(x) for x in r.stdout.split()]
+
+
+def test_num_splits_environment_override():
+    """SVLM_NUM_SPLITS replaces the planner's split count for calls that
+    leave it to the library (num_splits = 0), in the workspace queries as in
+    the launches (one planner); invalid values are ignored."""
+    auto, five, iauto, ifive = _workspace_in_subprocess("5")
+    assert auto == five > 0 and iauto == ifive > 0
+    default = _workspace_in_subprocess(None)
+    assert _workspace_in_subprocess("abc")[0] == default[0]
+    assert _workspace_in_subprocess("-3")[0] == default[0]
+    assert default[1] == five

@@ -32,6 +32,7 @@
 //    output) that a second kernel merges in split order.  Deterministic.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -705,6 +706,20 @@ struct Plan {
 
 constexpr int kMinStepsPerSplit = 2;  // shorter splits cost more in fixed latency than they add in parallelism
 
+// SVLM_NUM_SPLITS in the environment (a positive integer) replaces the
+// planner's split count for calls that leave it to the library
+// (num_splits = 0); read once per process.  0 when unset or invalid.
+int env_num_splits() {
+  static const int v = [] {
+    const char* e = std::getenv("SVLM_NUM_SPLITS");
+    if (!e || !*e) return 0;
+    char* end = nullptr;
+    const long n = std::strtol(e, &end, 10);
+    return (*end == 0 && n > 0 && n <= (1L << 20)) ? (int)n : 0;
+  }();
+  return v;
+}
+
 // max_steps_per_split > 0 caps the split length (indexed keys: the split's
 // list is staged in LDS).  64-bit throughout: the workspace queries take any
 // int sizes, and plan_fits() decides what can be launched.
@@ -718,7 +733,7 @@ Plan make_plan(int batch, int nq, int Hq, int Hkv, int D, int max_kv_len, int nu
   p.rb = ((rows + chunks - 1) / chunks + 15) / 16;
   p.row_chunks = (rows + p.rb * 16 - 1) / (p.rb * 16);
   const int64_t steps = ((int64_t)max_kv_len + kStep - 1) / kStep;
-  int64_t splits = num_splits;
+  int64_t splits = num_splits > 0 ? num_splits : env_num_splits();
   if (splits <= 0) {
     // Workgroups for about seven eighths of the compute units: the key loop
     // is bound by HBM bandwidth before every unit is busy, each extra split

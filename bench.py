@@ -457,7 +457,7 @@ def measure_batch_sweep(torch, ops, dev, g, steps, layers=8):
     row = Hkv * D * 2 * 2
     out = {}
     for kind, nq, N, batches in (("draft_attn", 1, cfg.budget + cfg.n_text + 1, (1, 2, 4, 8, 16, 32)),
-                                 ("verify_attn", cfg.gamma_verify + 1, cfg.n_ctx + cfg.gamma_verify + 1, (1, 2, 4))):
+                                 ("verify_attn", cfg.gamma_verify + 1, cfg.n_ctx + cfg.gamma_verify + 1, (1, 2, 4, 8, 16))):
         res = {}
         for B in batches:
             kvb = torch.empty(2, layers, B, Hkv, N, D, dtype=torch.bfloat16, device=dev)

@@ -135,6 +135,26 @@ def test_batch_with_ragged_lengths_and_strided_cache():
         assert np.abs(lse[b:b + 1] - rl).max() <= 1e-3
 
 
+@pytest.mark.parametrize("D,kv_len,splits", [(128, [9000, 300], 64), (128, [9000, 9000], 100), (64, [20000, 77], 100)])
+def test_many_splits_batched_merge(D, kv_len, splits):
+    """More partials per merge thread than one load round holds: the merge
+    takes them in batches and carries its reference maximum between them.
+    The short sequence leaves whole batches and whole split ranges empty."""
+    B, nq, Hq, Hkv = len(kv_len), 3, 8, 2
+    Ncap = max(kv_len)
+    q = _rand(71 + D, B, nq, Hq, D)
+    k = _rand(72 + D, B, Hkv, Ncap, D)
+    v = _rand(73 + D, B, Hkv, Ncap, D)
+    log(f"decode_attn case batched merge D={D} kv_len={kv_len} splits={splits}")
+    o, lse = _run(q, k, v, kv_len, True, num_splits=splits)
+    for b in range(B):
+        ro, rl = oracle.decode_attn(q[b:b + 1], k[b], v[b], [kv_len[b]], True)
+        err = row_rel_err(o[b:b + 1], ro)
+        log(f"  batch {b}: row-rel err {err:.2e}")
+        assert err <= REG_TOL
+        assert np.abs(lse[b:b + 1] - rl).max() <= 1e-3
+
+
 def test_verify_equals_sequential_draft_calls_on_gpu():
     """One dense pass over nq queries == nq single-query calls on the prefixes (same kernel family)."""
     nq, Hq, Hkv, D, N = 6, 16, 2, 128, 2500

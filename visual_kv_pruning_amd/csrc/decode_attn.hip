@@ -579,7 +579,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attn_splitk(AttnArgs a) {
 // Merge launch: kCombineRows rows per workgroup, 128 threads per row = D/4
 // column groups x (512/D) split parts.  With at most SPAN splits per part, a
 // thread loads all of its (max, sum, output) partials at once — one memory
-// round trip — and merges them in split order; SPAN = 0 loops over any number.
+// round trip — and merges them in split order; SPAN = 0 takes any number, in
+// batches of kCombineSpan, one round trip each.
 // The parts are then combined in a fixed order through LDS.  Deterministic.
 constexpr int kCombineRows = 2;
 constexpr int kCombineSpan = 8;
@@ -628,19 +629,39 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
         }
       }
     } else {
-      for (int sp = s_lo; sp < s_hi; ++sp) M = fmaxf(M, ml[sp].x);
-      if (M != kNegInf) {
-#pragma unroll 8
-        for (int sp = s_lo; sp < s_hi; ++sp) {
-          const float2 st = ml[sp];
-          const float4 v = po[(int64_t)sp * C4];
-          const float w = (st.x == kNegInf) ? 0.f : exp2f(st.x - M);
-          L += w * st.y;
-          acc.x += w * v.x;
-          acc.y += w * v.y;
-          acc.z += w * v.z;
-          acc.w += w * v.w;
+      // batches of kCombineSpan partials, each loaded at once and joined to
+      // the running (M, L, acc): the batch's largest maximum first, then
+      // every partial weighed against the new reference
+      for (int s0 = s_lo; s0 < s_hi; s0 += kCombineSpan) {
+        float2 st[kCombineSpan];
+        float4 v[kCombineSpan];
+#pragma unroll
+        for (int i = 0; i < kCombineSpan; ++i) {
+          const int sp = s0 + i;
+          st[i] = (sp < s_hi) ? ml[sp] : make_float2(kNegInf, 0.f);
+          v[i] = (sp < s_hi) ? po[(int64_t)sp * C4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        float bm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < kCombineSpan; ++i) bm = fmaxf(bm, st[i].x);
+        const float m_new = fmaxf(M, bm);
+        if (m_new == kNegInf) continue;
+        const float f = (M == kNegInf) ? 0.f : exp2f(M - m_new);
+        L *= f;
+        acc.x *= f;
+        acc.y *= f;
+        acc.z *= f;
+        acc.w *= f;
+#pragma unroll
+        for (int i = 0; i < kCombineSpan; ++i) {
+          const float w = (st[i].x == kNegInf) ? 0.f : exp2f(st[i].x - m_new);
+          L += w * st[i].y;
+          acc.x += w * v[i].x;
+          acc.y += w * v[i].y;
+          acc.z += w * v[i].z;
+          acc.w += w * v[i].w;
+        }
+        M = m_new;
       }
     }
   }

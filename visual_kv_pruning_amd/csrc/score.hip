@@ -501,6 +501,8 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
   }
 }
 
+constexpr int kAggBatch = 16;
+
 // final mean over the group sums (KV-head rows split over several workgroups,
 // or the single all-head row), out = alpha * mean + beta * out
 __global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
@@ -518,11 +520,23 @@ __global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
     nr = a.Hkv * a.HG2;
     div = (float)a.Hq;
   }
-  float acc = 0.f;
-  for (int k = 0; k < nr; ++k) acc += a.grp[(int64_t)(r0 + k) * a.n_vis + i];
-  const float v = acc / div;
   float* o = a.out + (int64_t)r * a.n_vis + i;
-  *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * (*o);
+  const float prev = (a.beta == 0.f) ? 0.f : *o;
+  // the group sums are loaded kAggBatch at a time, every load of a batch
+  // issued before the first add (rows past the last are clamped to it and
+  // not added); the adds keep row order
+  float acc = 0.f;
+  const float* g = a.grp + i;
+  for (int k0 = 0; k0 < nr; k0 += kAggBatch) {
+    float x[kAggBatch];
+#pragma unroll
+    for (int j = 0; j < kAggBatch; ++j) x[j] = g[(int64_t)(r0 + min(k0 + j, nr - 1)) * a.n_vis];
+#pragma unroll
+    for (int j = 0; j < kAggBatch; ++j)
+      if (k0 + j < nr) acc += x[j];
+  }
+  const float v = acc / div;
+  *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * prev;
 }
 
 // (g, s) pairs in groups of 8 (one per XCD), times the head groups

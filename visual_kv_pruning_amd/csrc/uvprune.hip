@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxDim = 16384;  // the two fp32 text sums (2 x 64 KB) fit in LDS
+constexpr int kLoadBatch = 4;   // text-row chunks per thread in flight (text norms)
 
 struct UvArgs {
   const uint16_t* v0;
@@ -59,14 +60,25 @@ __device__ __forceinline__ float inv_norm(float sumsq) { return sumsq > 0.f ? 1.
 __global__ __launch_bounds__(kThreads) void text_norms(UvArgs a) {
   const int j = blockIdx.x, layer = blockIdx.y;
   const uint16_t* row = (layer ? a.xL : a.x0) + (int64_t)j * a.x_sn;
+  // kLoadBatch chunks per thread in flight, summed in the order of a plain loop
+  const int nc = a.d / 8;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < a.d / 8; c += kThreads) {
-    const u32x4 w = *(const u32x4*)(row + 8 * c);
+  for (int c0 = threadIdx.x; c0 < nc; c0 += kThreads * kLoadBatch) {
+    u32x4 w[kLoadBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf16_lo(w[e]), hi = bf16_hi(w[e]);
-      ss = fmaf(lo, lo, ss);
-      ss = fmaf(hi, hi, ss);
+    for (int u = 0; u < kLoadBatch; ++u) {
+      const int c = c0 + u * kThreads;
+      w[u] = (c < nc) ? *(const u32x4*)(row + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+      if (c0 + u * kThreads >= nc) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(w[u][e]), hi = bf16_hi(w[u][e]);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
     }
   }
   ss = wave_sum(ss);
@@ -109,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void text_sums(UvArgs a) {
 
 // one wave per video row: |V^0_i|^2, <V^0_i, xbar^0>, |V^L_i|^2, <V^L_i, xbar^L>
 constexpr int kRowUnroll = 8;  // 16-byte chunks per lane in flight per layer
+constexpr int kXbarBatch = 16; // text-sum loads per thread in flight when LDS is filled
 
 __device__ __forceinline__ void row_chunk(const u32x4& w0, const u32x4& wL, const float4* xb, int d4, int c,
                                           float& ss0, float& dt0, float& ssL, float& dtL) {
@@ -134,7 +147,20 @@ __device__ __forceinline__ void row_chunk(const u32x4& w0, const u32x4& wL, cons
 __global__ __launch_bounds__(kThreads) void video_scores(UvArgs a) {
   extern __shared__ float4 sm_xbar[];  // [2][d / 4]
   const int d4 = a.d / 4;
-  for (int k = threadIdx.x; k < 2 * d4; k += kThreads) sm_xbar[k] = ((const float4*)a.xbar)[k];
+  // the text sums into LDS, kXbarBatch loads per thread in flight
+  for (int k0 = threadIdx.x; k0 < 2 * d4; k0 += kThreads * kXbarBatch) {
+    float4 t[kXbarBatch];
+#pragma unroll
+    for (int u = 0; u < kXbarBatch; ++u) {
+      const int k = k0 + u * kThreads;
+      t[u] = (k < 2 * d4) ? ((const float4*)a.xbar)[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kXbarBatch; ++u) {
+      const int k = k0 + u * kThreads;
+      if (k < 2 * d4) sm_xbar[k] = t[u];
+    }
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int waves = gridDim.x * (kThreads / 64);

@@ -242,12 +242,20 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
   __shared__ uint64_t s_w[kThreads / 64], s_p[kThreads / 64];
   __shared__ ArgMax s_a[kThreads / 64];
   if (tid == 0) sm_n = a.r_first[b];
-  // row totals over the chunks (chunk-parallel; integer sums are exact in any order)
-  uint64_t mw = 0, mp = 0;
+  const double uu = a.u[(int64_t)b * (G + 1) + G];  // in flight with the chunk results
+  // row totals over the chunks (chunk-parallel; integer sums are exact in any
+  // order); a thread keeps the masses of its first chunk for the ordered scan
+  uint64_t mw = 0, mp = 0, first_w = 0, first_p = 0;
   ArgMax best = {-INFINITY, 0x7fffffff};
   for (int c = tid; c < a.chunks; c += kThreads) {
-    mw += a.r_mass[((int64_t)b * a.chunks + c) * 2 + 0];
-    mp += a.r_mass[((int64_t)b * a.chunks + c) * 2 + 1];
+    const uint64_t xw = a.r_mass[((int64_t)b * a.chunks + c) * 2 + 0];
+    const uint64_t xp = a.r_mass[((int64_t)b * a.chunks + c) * 2 + 1];
+    if (c == tid) {
+      first_w = xw;
+      first_p = xp;
+    }
+    mw += xw;
+    mp += xp;
     best = better(best, a.r_arg[(int64_t)b * a.chunks + c]);
   }
   mw = wave_sum_u64(mw);
@@ -272,7 +280,6 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
   const uint64_t W = (mode0 == 0) ? Ww : Wp;
   uint64_t t = 0;
   if (mode0 < 2) {
-    const double uu = a.u[(int64_t)b * (G + 1) + G];
     t = (uint64_t)floor(uu * (double)W);
     if (t > W - 1) t = W - 1;
   }
@@ -288,7 +295,10 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
     uint64_t carry = 0;
     for (int c0 = 0; c0 < a.chunks; c0 += kThreads) {
       const int c = c0 + tid;
-      const uint64_t m = (c < a.chunks) ? a.r_mass[((int64_t)b * a.chunks + c) * 2 + mode0] : 0ull;
+      // the first round's masses are already in registers
+      const uint64_t m = (c >= a.chunks) ? 0ull
+                         : (c0 == 0)     ? ((mode0 == 0) ? first_w : first_p)
+                                         : a.r_mass[((int64_t)b * a.chunks + c) * 2 + mode0];
       uint64_t incl = m;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {

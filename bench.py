@@ -4,7 +4,7 @@
 One step = one pass of the whole hot path over one synthetic request:
   score (80 layers, mean text->visual attention averaged into one row)
   -> select (Top-P 0.5 + spatially uniform fill to 10% = 2509 tokens)
-  -> gather (80 layers: kept visual + 128 text rows into the draft cache)
+  -> gather (all 80 layers in one call: kept visual + 128 text rows into the draft cache)
   -> draft decode attention (80 layers, 1 query over 2638 keys)
   -> dense verify decode attention (80 layers, gamma+1 = 6 queries over 25222 keys)
   -> acceptance (rejection sampling, gamma 5, vocabulary 152064).
@@ -124,6 +124,7 @@ def main():
 
     row = torch.empty(1, NV, dtype=torch.float32, device=dev)
     ws_score = torch.empty(ops.score_workspace_bytes(T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
+    ws_score_l = torch.empty(ops.score_layers_workspace_bytes(L, T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, nqv, Hq, Hkv, D, N_full)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(256, ops.decode_attn_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)), dtype=torch.uint8, device=dev)
     ws_di = torch.empty(max(256, ops.decode_attn_indexed_workspace_bytes(1, 1, Hq, Hkv, D, N_draft)),
@@ -152,15 +153,27 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    def k_score(l):
+    def k_score():
+        # every layer in one call: the mean over layers and heads into one row
+        ops.score_layers(qt, K, NV, NV, agg="all", layer_mean=True, out=row, ws=ws_score_l)
+
+    def k_score_layer(l):
         ops.score(qt[l], K[l], NV, NV, agg="all", alpha=1.0 / L, beta=0.0 if l == 0 else 1.0, out=row, ws=ws_score)
 
     def k_select():
         kept_box["kept"] = ops.select(row, cfg.frames, cfg.gh, cfg.gw, cfg.top_p, B_keep)[0]
         draft_idx[:B_keep].copy_(kept_box["kept"][0])
 
-    def k_gather(l):
-        ops.gather_kv(K[l], Vv[l], kept_box["kept"][0], NV, T, draft_kv[0, l, :, :B_keep + T], draft_kv[1, l, :, :B_keep + T])
+    # one call gathers every layer: the layers' caches fold into the head axis
+    # (uniform strides), and the selection row is shared by all of them
+    K_all = K.reshape(L * Hkv, N_full, D)
+    V_all = Vv.reshape(L * Hkv, N_full, D)
+    dk_all = draft_kv[0, :, :, :B_keep + T].reshape(L * Hkv, B_keep + T, D)
+    dv_all = draft_kv[1, :, :, :B_keep + T].reshape(L * Hkv, B_keep + T, D)
+    assert dk_all.data_ptr() == draft_kv[0].data_ptr() and dk_all.stride(0) == N_draft * D
+
+    def k_gather():
+        ops.gather_kv(K_all, V_all, kept_box["kept"][0], NV, T, dk_all, dv_all)
 
     def k_draft(l):
         ops.decode_attn(qd[l], draft_kv[0, l], draft_kv[1, l], kv_len_d, False, out=o_d, lse=l_d, ws=ws_d)
@@ -178,16 +191,17 @@ def main():
         ops.verify("reject", d_t, p_t, q_t, u_t, ws=ws_acc)
 
     seqs = {
-        "score": lambda: [k_score(l) for l in range(L)],
+        "score": k_score,
+        "score_layer_calls": lambda: [k_score_layer(l) for l in range(L)],
         "select": k_select,
-        "gather": lambda: [k_gather(l) for l in range(L)],
+        "gather": k_gather,
         "draft_attn": lambda: [k_draft(l) for l in range(L)],
         "draft_attn_indexed": lambda: [k_draft_idx(l) for l in range(L)],
         "uvprune_score": k_uvprune,
         "verify_attn": lambda: [k_verify_attn(l) for l in range(L)],
         "accept": k_accept,
     }
-    calls = {"score": L, "select": 1, "gather": L, "draft_attn": L, "draft_attn_indexed": L, "uvprune_score": 1,
+    calls = {"score": 1, "score_layer_calls": L, "select": 1, "gather": 1, "draft_attn": L, "draft_attn_indexed": L, "uvprune_score": 1,
              "verify_attn": L, "accept": 1}
 
     # warm up eagerly (also fills the library's device-property cache), then capture
@@ -207,7 +221,7 @@ def main():
     # one step of the path: every kind but the alternatives, timed on their own
     # below (the in-place draft instead of gather + compact draft; the UV-Prune
     # score instead of the attention score)
-    step_kinds = [k for k in seqs if k not in ("draft_attn_indexed", "uvprune_score")]
+    step_kinds = [k for k in seqs if k not in ("draft_attn_indexed", "uvprune_score", "score_layer_calls")]
 
     def step():
         for kind in step_kinds:
@@ -319,15 +333,21 @@ def main():
     kernels["uvprune_score"].update(
         bytes=uv_bytes, gbs=round(uv_bytes / (per_us["uvprune_score"] * 1e-6) / 1e9, 1),
         what="UV-Prune score from layer-0 and layer-L hidden states (hidden 8192), once per prefill")
-    kernels["score"].update(flop=score_flop, tflops=round(score_flop / (us_score * 1e-6) / 1e12, 1))
+    kernels["score"].update(flop=L * score_flop, tflops=round(L * score_flop / (us_score * 1e-6) / 1e12, 1),
+                            us_per_layer=round(us_score / L, 3),
+                            what="svlm_score_layers: all 80 layers in one call, averaged into one row")
+    kernels["score_layer_calls"].update(
+        flop=score_flop, tflops=round(score_flop / (per_us["score_layer_calls"] * 1e-6) / 1e12, 1),
+        what="the same score as 80 svlm_score calls (one per layer, accumulated with alpha/beta)")
     # acceptance: the gamma test probabilities, then the one row (p_n and q_n, or the bonus row p_gamma)
     # the draw scans; latency-bound (two launches, dependent loads)
     acc_bytes = 2 * V * 4
     kernels["accept"].update(bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept"] * 1e-6) / 1e9, 1),
                              what="rejection acceptance, gamma 5, V 152064: bytes = the two probability rows "
                                   "the draw reads (p_n and q_n); two launches of dependent loads")
-    kernels["gather"].update(bytes=2 * 2 * (B_keep + T) * Hkv * D * 2,
-                             gbs=round(2 * 2 * (B_keep + T) * Hkv * D * 2 / (per_us["gather"] * 1e-6) / 1e9, 1))
+    gather_bytes = L * 2 * 2 * (B_keep + T) * Hkv * D * 2  # every layer's kept K and V rows, read + write
+    kernels["gather"].update(bytes=gather_bytes, gbs=round(gather_bytes / (per_us["gather"] * 1e-6) / 1e9, 1),
+                             what="one call over all layers (their caches folded into the head axis)")
 
     result = {
         "metric": METRIC,
@@ -510,12 +530,16 @@ def measure_other_shapes(torch, ops, dev, g, steps):
         us_d = graph_us(torch, lambda: [ops.decode_attn(qv[l][:, :1], kv[0, l, :, :Nd], kv[1, l, :, :Nd], kld,
                                                         False, out=o[:, :1], lse=lse[:, :1], ws=wsd)
                                         for l in range(layers)], layers, steps)
-        rows_out = {"all": 1, "layer": 1, "layer_kvhead": Hkv}[cfg.rows]
+        # the shape's selection rows (one averaged row, one per layer, or one per
+        # (layer, KV head)) from every rotated layer in one call
         agg = "kvhead" if cfg.rows == "layer_kvhead" else "all"
-        srow = torch.empty(rows_out, NV, device=dev)
-        wss = torch.empty(ops.score_workspace_bytes(T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
-        us_s = graph_us(torch, lambda: [ops.score(qt[l], kv[0, l, :, :NV + T], NV, NV, agg=agg, out=srow, ws=wss)
-                                        for l in range(layers)], layers, max(2, steps // 2))
+        mean = cfg.rows == "all"
+        kl = kv[0, :, :, :NV + T]
+        wss = torch.empty(ops.score_layers_workspace_bytes(layers, T, Hq, Hkv, NV, NV), dtype=torch.uint8,
+                          device=dev)
+        srow = ops.score_layers(qt, kl, NV, NV, agg=agg, layer_mean=mean, ws=wss)
+        us_s = graph_us(torch, lambda: ops.score_layers(qt, kl, NV, NV, agg=agg, layer_mean=mean, out=srow, ws=wss),
+                        layers, max(2, steps // 2))
         flop = 2 * D * Hq * (T * NV + T * (T + 1) // 2) + 2 * D * Hq * T * NV
         out[cfg.name] = {
             "verify_attn": {"us_avg": round(us_v, 3), "bytes": Nv * row, "keys": Nv, "queries": nq,

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SVLM_ABI_VERSION 3
+#define SVLM_ABI_VERSION 4
 
 enum svlm_status {
   SVLM_OK = 0,
@@ -126,6 +126,39 @@ int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh,
                int Hq, int Hkv, int D, float scale, int agg,
                float alpha, float beta, float* out,
                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * svlm_score_layers - svlm_score over `layers` layers in one call.
+ * [SpecVLM-5]; [StD-sel] (the selection signal averaged over layers and
+ * heads, or kept per layer).
+ *
+ * Layer l reads q_text + l*q_sl and k + l*k_sl (element strides, multiples
+ * of 16 bytes, >= 0); every other argument is as for svlm_score, the same
+ * for every layer.  Let R_l = agg(A_l), the rows svlm_score would form for
+ * layer l (Hq, Hkv or 1 rows of n_vis).
+ *   layer_mean = 1: out = alpha * (1/layers) * sum_l R_l + beta * out,
+ *                   rows as for one layer (agg SVLM_AGG_KVHEAD or
+ *                   SVLM_AGG_ALL; SVLM_AGG_QHEAD is SVLM_E_UNSUPPORTED).
+ *   layer_mean = 0: out[l] = alpha * R_l + beta * out[l], out is
+ *                   [layers][rows][n_vis].
+ * With layers == 1 it is svlm_score (bit for bit, either layer_mean).
+ * The layers share the launches: the key splits are planned over all of
+ * them (about four rounds of workgroups over the chip), so each workgroup
+ * covers more keys than in a one-layer call and the results differ from
+ * per-layer svlm_score calls by fp32 reordering only.
+ * ws: svlm_score_layers_workspace(layers, T, Hq, Hkv, q_pos0, n_vis) bytes
+ *     (the per-layer statistics and group rows of every layer).
+ * Errors as svlm_score; layers < 1 or layer_mean outside {0, 1} is
+ * SVLM_E_INVALID; sizes whose launches or workspace exceed the limits are
+ * SVLM_E_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+size_t svlm_score_layers_workspace(int layers, int T, int Hq, int Hkv, int q_pos0, int n_vis);
+int svlm_score_layers(const void* q_text, int64_t q_st, int64_t q_sh, int64_t q_sl,
+                      const void* k, int64_t k_sh, int64_t k_sn, int64_t k_sl, int layers,
+                      int dtype, int T, int n_ctx, int q_pos0, int vis_start, int n_vis,
+                      int Hq, int Hkv, int D, float scale, int agg, int layer_mean,
+                      float alpha, float beta, float* out,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * svlm_select - two-stage visual token selection, one row at a time.

@@ -53,6 +53,8 @@ int main(void) {
     if (svlm_score_workspace(M, M, 1, 0, M) != 0) ++fails;
     if (svlm_score_workspace(16, M, M, M, M) != 0) ++fails;
     (void)svlm_score_workspace(128, M, M, M - 128, 1 << 18);
+    (void)svlm_score_layers_workspace(M, 128, M, M, M - 128, 1 << 18);
+    (void)svlm_score_layers_workspace(M, 128, 64, 8, M - 128, 1 << 18);
     if (svlm_select_workspace(M, M, M, 0.5) != 0) ++fails;
     if (svlm_select_workspace(M, M, 1, 1.0) != 0) ++fails;
     if (svlm_select_workspace(M, 1 << 18, 1024, 1.0) != 0) ++fails;
@@ -78,6 +80,16 @@ int main(void) {
                     1 << 20, 0), SVLM_E_INVALID, "score scale");
   expect(svlm_score(f, 256, 64, f, 212 * 64, 64, SVLM_F32, 16, 212, 196, 0, 196, 4, 2, 64, 0.125f, 2, 1, 0, ff, f,
                     16, 0), SVLM_E_WORKSPACE, "score workspace");
+
+  expect(svlm_score_layers(f, 256, 64, 1 << 16, f, 212 * 64, 64, 212 * 128, 0, SVLM_BF16, 16, 212, 196, 0, 196, 4,
+                           2, 64, 0.125f, 2, 1, 1, 0, ff, f, 1 << 20, 0), SVLM_E_INVALID, "score layers count");
+  expect(svlm_score_layers(f, 256, 64, 1 << 16, f, 212 * 64, 64, 212 * 128, 3, SVLM_BF16, 16, 212, 196, 0, 196, 4,
+                           2, 64, 0.125f, 2, 1, 1, 0, ff, f, 16, 0), SVLM_E_WORKSPACE, "score layers workspace");
+  if (svlm_score_layers_workspace(-1, 16, 4, 2, 196, 196) != 0 ||
+      svlm_score_layers_workspace(1, 16, 4, 2, 196, 196) != svlm_score_workspace(16, 4, 2, 196, 196)) {
+    fprintf(stderr, "score layers workspace query\n");
+    ++fails;
+  }
 
   /* select */
   expect(svlm_select((const float*)f, 20, 1, 2, 2, 5, 0.5, 21, fi, fi, 0, 0, 0, 0), SVLM_E_INVALID, "select budget");

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svlm_abi_version() == L.ABI_VERSION == 3
+    assert lib.svlm_abi_version() == L.ABI_VERSION == 4
     for st in range(5):
         assert lib.svlm_status_string(st)
     assert b"unknown" in lib.svlm_status_string(99)
@@ -190,6 +190,19 @@ def test_verify_select_gather_score_reject_bad_arguments(lib):
     args[16] = 2
     args[1] = 1 << 27                        # one head's queries past a 32-bit buffer range
     assert lib.svlm_score(*args) == L.SVLM_E_UNSUPPORTED
+    # score_layers: layer count, layer-mean flag, per-head rows under the layer
+    # mean, a short workspace; the workspace of one layer is svlm_score's
+    la = [fake, 1024, 128, 1 << 20, fake, 1 << 16, 128, 1 << 22, 2, 0, 16, 300, 100, 0, 50, 8, 2, 128, 0.1, 2, 1,
+          1.0, 0.0, fake, fake, 1 << 30, NULL]
+    for i, val, want in ((8, 0, L.SVLM_E_INVALID), (20, 2, L.SVLM_E_INVALID), (19, 0, L.SVLM_E_UNSUPPORTED),
+                         (25, 16, L.SVLM_E_WORKSPACE), (3, 3, L.SVLM_E_INVALID)):
+        bad = list(la)
+        bad[i] = val
+        assert lib.svlm_score_layers(*bad) == want, (i, val)
+    one = lib.svlm_score_workspace(16, 8, 2, 100, 50)
+    assert lib.svlm_score_layers_workspace(1, 16, 8, 2, 100, 50) == one > 0
+    assert lib.svlm_score_layers_workspace(3, 16, 8, 2, 100, 50) >= 3 * one
+    assert lib.svlm_score_layers_workspace(0, 16, 8, 2, 100, 50) == 0
 
 
 def test_noalloc_refuses_state_beyond_its_scratch_on_the_host(lib):

@@ -30,6 +30,31 @@ def test_gather_matches_indexing(D, per_head):
     assert np.array_equal(vd.float().cpu().numpy(), rv)
 
 
+def test_all_layers_in_one_call():
+    """Layers folded into the head axis ([L][Hkv] -> L*Hkv heads, uniform
+    strides) gather every layer's kept rows in one call, into a destination
+    with room for more rows per head (the draft cache), as bench.py does."""
+    from visual_kv_pruning_amd import ops
+    L, Hkv, N, D, T, n_idx, n_cap = 5, 4, 2000, 128, 16, 203, 240
+    rng = np.random.default_rng(17)
+    kv = W.bf16_round(rng.standard_normal((2, L, Hkv, N, D)).astype(np.float32))
+    idx = np.sort(rng.choice(N - T, n_idx, replace=False)).astype(np.int32)
+    kvd = dev_bf16(kv)
+    dst = torch.zeros(2, L, Hkv, n_cap, D, dtype=torch.bfloat16, device="cuda:0")
+    log(f"gather case all layers in one call L={L}")
+    n = n_idx + T
+    dk, dv = dst[0, :, :, :n].reshape(L * Hkv, n, D), dst[1, :, :, :n].reshape(L * Hkv, n, D)
+    assert dk.data_ptr() == dst[0].data_ptr() and dk.stride(0) == n_cap * D  # views, not copies
+    ops.gather_kv(kvd[0].reshape(L * Hkv, N, D), kvd[1].reshape(L * Hkv, N, D), torch.from_numpy(idx).cuda(),
+                  N - T, T, dk, dv)
+    torch.cuda.synchronize()
+    got = dst.float().cpu().numpy()
+    for l in range(L):
+        for t in range(2):
+            assert np.array_equal(got[t, l, :, :n], oracle.gather_kv(kv[t, l], idx, N - T, T)), (l, t)
+    assert not got[:, :, :, n:].any()  # rows past the gathered ones untouched
+
+
 def test_gather_into_strided_destination_and_empty():
     from visual_kv_pruning_amd import ops
     k, v = W.random_kv(4, 2, 500, 128)

@@ -237,3 +237,107 @@ def test_tiny_config_fp32_operands(agg):
     ref = _ref(p, cfg, agg)
     _compare(out.cpu().numpy(), ref, f"tiny fp32/{agg}", rel_tol=F32_REL_TOL)
     _compare(out2.cpu().numpy(), 0.75 * ref, f"tiny fp32/{agg} alpha beta", rel_tol=F32_REL_TOL)
+
+
+# ---------------------------------------------------------------------------
+# svlm_score_layers: every layer in one call
+
+
+def _stack_layers(cfg, n):
+    ps = [W.prefill_layer(cfg, l) for l in range(n)]
+    return ps, np.stack([p.q_text for p in ps]), np.stack([p.k for p in ps])
+
+
+@pytest.mark.parametrize("cfg,n", [(W.C1, 5), (W.C2, 3)], ids=["tiny5", "qwen2vl7b3"])
+@pytest.mark.parametrize("rows", ["all", "layer", "layer_kvhead", "kvhead_mean"])
+def test_layers_in_one_call_match_oracle_rows(cfg, n, rows):
+    """One call over n layers against the oracle's multi-layer rows: the
+    single row averaged over layers and heads, one row per layer, one row
+    per (layer, KV head), and the per-KV-head rows averaged over layers."""
+    from visual_kv_pruning_amd import ops
+    ps, q, k = _stack_layers(cfg, n)
+    agg = "kvhead" if rows in ("layer_kvhead", "kvhead_mean") else "all"
+    mean = rows in ("all", "kvhead_mean")
+    log(f"score_layers case {cfg.name} x{n} {rows}")
+    out = ops.score_layers(dev_bf16(q), dev_bf16(k), ps[0].q_pos0, cfg.n_vis, agg=agg, layer_mean=mean)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, cfg.n_vis)
+    if rows == "kvhead_mean":
+        ref = np.mean([_ref(p, cfg, "kvhead") for p in ps], axis=0)
+    else:
+        ref = oracle.score_rows_for_config([(p.q_text, p.k) for p in ps], ps[0].q_pos0, cfg.n_vis, cfg.hkv, rows)
+    _compare(got, ref, f"{cfg.name} x{n} {rows}")
+
+
+def test_layers_alpha_beta():
+    """out = alpha * (layer mean) + beta * out."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C1
+    ps, q, k = _stack_layers(cfg, 3)
+    prev = np.random.default_rng(2).random((1, cfg.n_vis)).astype(np.float32) * 1e-3
+    out = torch.from_numpy(prev).cuda()
+    log("score_layers case alpha/beta")
+    ops.score_layers(dev_bf16(q), dev_bf16(k), ps[0].q_pos0, cfg.n_vis, agg="all", layer_mean=True,
+                     alpha=0.25, beta=2.0, out=out)
+    torch.cuda.synchronize()
+    ref = 0.25 * oracle.score_rows_for_config([(p.q_text, p.k) for p in ps], ps[0].q_pos0, cfg.n_vis, cfg.hkv,
+                                              "all") + 2.0 * prev
+    _compare(out.cpu().numpy(), ref, "tiny x3 alpha/beta")
+
+
+@pytest.mark.parametrize("agg", ["qhead", "kvhead", "all"])
+def test_one_layer_call_is_svlm_score(agg):
+    """layers = 1 runs svlm_score's launches: bit-identical rows, with or
+    without the layer mean."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C2
+    p = W.prefill_layer(cfg, 0)
+    qd, kd = dev_bf16(p.q_text), dev_bf16(p.k)
+    log(f"score_layers case one layer {agg}")
+    a = ops.score(qd, kd, p.q_pos0, cfg.n_vis, agg=agg)
+    b = ops.score_layers(qd[None], kd[None], p.q_pos0, cfg.n_vis, agg=agg, layer_mean=False)
+    c = ops.score_layers(qd[None], kd[None], p.q_pos0, cfg.n_vis, agg=agg, layer_mean=agg != "qhead")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b[0]) and torch.equal(a, c.reshape(a.shape))
+
+
+def test_llava72b_four_layers_sampled_kv_head():
+    """Four full 72B-shape layers in one call, rows per KV head averaged over
+    the layers; the oracle checks KV head 0 (its 8 q heads, every layer)."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C3
+    ps, q, k = _stack_layers(cfg, 4)
+    log("score_layers case 72B x4, KV head 0")
+    out = ops.score_layers(dev_bf16(q), dev_bf16(k), ps[0].q_pos0, cfg.n_vis, agg="kvhead", layer_mean=True)
+    torch.cuda.synchronize()
+    G = cfg.group
+    ref = np.mean([oracle.aggregate_heads(oracle.score_layer(p.q_text[:, :G], p.k[:1], p.q_pos0, 0, cfg.n_vis, 1),
+                                          1, "kvhead") for p in ps], axis=0)
+    _compare(out.cpu().numpy()[:1], ref, "72B x4 kv head 0")
+
+
+def test_llava72b_eighty_layers_equal_per_layer_calls():
+    """The launch bench.py times: all 80 layers of the 72B shape in one call,
+    against the mean of 80 svlm_score calls (each pinned to the oracle above);
+    the two differ by fp32 summation order only.  Repeated calls are
+    bit-identical."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C3
+    L, T, Hq, Hkv, D, NV = cfg.layers, cfg.n_text, cfg.hq, cfg.hkv, cfg.d, cfg.n_vis
+    g = torch.Generator(device="cuda:0").manual_seed(9)
+    k = torch.empty(L, Hkv, cfg.n_ctx, D, dtype=torch.bfloat16, device="cuda:0")
+    for l in range(L):
+        k[l].copy_(torch.randn(Hkv, cfg.n_ctx, D, generator=g, device="cuda:0"))
+    q = torch.randn(L, T, Hq, D, generator=g, device="cuda:0").to(torch.bfloat16)
+    log("score_layers case 72B x80 vs per-layer calls")
+    per = torch.empty(1, NV, device="cuda:0")
+    for l in range(L):
+        ops.score(q[l], k[l], NV, NV, agg="all", alpha=1.0 / L, beta=0.0 if l == 0 else 1.0, out=per)
+    one = ops.score_layers(q, k, NV, NV, agg="all", layer_mean=True)
+    again = ops.score_layers(q, k, NV, NV, agg="all", layer_mean=True)
+    torch.cuda.synchronize()
+    assert torch.equal(one, again)
+    a, b = one.cpu().numpy().astype(np.float64), per.cpu().numpy().astype(np.float64)
+    rel = float((np.abs(a - b) / np.abs(b)).max())
+    log(f"  max relative difference {rel:.2e}")
+    assert rel <= 1e-5

@@ -31,6 +31,9 @@ SIGNATURES = {
     "svlm_score_workspace": (sz, [i32, i32, i32, i32, i32]),
     "svlm_score": (i32, [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                          f32, i32, f32, f32, vp, vp, sz, vp]),
+    "svlm_score_layers_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
+    "svlm_score_layers": (i32, [vp, i64, i64, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                i32, f32, i32, i32, f32, f32, vp, vp, sz, vp]),
     "svlm_select_workspace": (sz, [i32, i32, i32, f64]),
     "svlm_select": (i32, [vp, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, sz, vp]),
     "svlm_gather_kv": (i32, [vp, vp, i64, i64, i32, vp, i64, i32, i32, i32, vp, vp, i64, i64, i32, i32, i32, vp]),
@@ -50,7 +53,7 @@ SIGNATURES = {
     "svlm_debug_flags": (i32, [C.POINTER(C.c_uint)]),
 }
 
-ABI_VERSION = 3  # SVLM_ABI_VERSION of include/svlm.h
+ABI_VERSION = 4  # SVLM_ABI_VERSION of include/svlm.h
 
 _lib = None
 _debug_lib = None

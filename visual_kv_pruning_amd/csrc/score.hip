@@ -49,19 +49,42 @@ struct ScoreArgs {
   int agg;
   float alpha, beta;
   float* out;
+  // several layers per call: workgroups of layer l follow those of layer l-1
+  int layers;             // 1 for svlm_score
+  int64_t q_sl, k_sl;     // per-layer element strides of q and k
+  int64_t ws_sl;          // per-layer float stride of both workspace parts (ml and grp)
+  int layer_mean;         // 1: the layers are averaged into one row set (score_agg_layers)
+  int rows;               // output rows per layer (by agg)
 };
 
-// block id -> (KV head g, head group hg, key split s).  Workgroups are handed
-// to the eight XCDs round-robin by id, so the HG head groups of one (KV head,
-// split) take ids 8 apart: they run on one XCD, and the K tiles one of them
-// fetches reach the others from that XCD's L2.  Ids past the last (g, s) pair
-// of a partial group of eight are idle.
-__device__ __forceinline__ bool decode_block(int S, int Hkv, int HG, int& g, int& hg, int& s) {
-  const int bid = blockIdx.x;
+// the arguments as seen by one layer's workgroups: inputs, workspace and (one
+// row set per layer) output moved to that layer
+__device__ __forceinline__ ScoreArgs layer_args(const ScoreArgs& a0, int layer) {
+  ScoreArgs a = a0;
+  a.q += layer * a0.q_sl;
+  a.k += layer * a0.k_sl;
+  a.ml += layer * a0.ws_sl;
+  a.grp += layer * a0.ws_sl;
+  if (!a0.layer_mean) a.out += (int64_t)layer * a0.rows * a0.n_vis;
+  return a;
+}
+
+// block id -> (layer, KV head g, head group hg, key split s).  Workgroups are
+// handed to the eight XCDs round-robin by id, so the HG head groups of one
+// (layer, KV head, split) take ids 8 apart: they run on one XCD, and the K
+// tiles one of them fetches reach the others from that XCD's L2.  The
+// (layer, g, s) triples are numbered across layers, so only the last group
+// of eight can be partial (its missing ids are idle) and every XCD gets an
+// equal share.
+__device__ __forceinline__ bool decode_block(int bid, int S, int Hkv, int HG, int layers, int& layer, int& g,
+                                             int& hg, int& s) {
   const int rest = bid >> 3;
   hg = rest % HG;
-  const int pair = (rest / HG) * 8 + (bid & 7);
-  if (pair >= Hkv * S) return false;
+  const int trip = (rest / HG) * 8 + (bid & 7);
+  const int per_layer = Hkv * S;
+  if (trip >= layers * per_layer) return false;
+  layer = trip / per_layer;
+  const int pair = trip - layer * per_layer;
   s = pair % S;
   g = pair / S;
   return true;
@@ -217,14 +240,15 @@ __device__ __forceinline__ void load_q(const ScoreArgs& a, int h, u32x4 (&q)[RB]
 }
 
 template <int D, int RB, int W, int NS>
-__global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
+__global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   constexpr int KK = D / 32;
   using Ring = KRing<D, W, NS>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g4 = lane >> 4;
-  int g, hg, s;
-  if (!decode_block(a.S1, a.Hkv, a.HG1, g, hg, s)) return;
+  int layer, g, hg, s;
+  if (!decode_block((int)blockIdx.x, a0.S1, a0.Hkv, a0.HG1, a0.layers, layer, g, hg, s)) return;
+  const ScoreArgs a = layer_args(a0, layer);
   const int hl = hg * W + wave;  // head within the KV group; waves past the group compute but do not write
   const int h = g * a.G + min(hl, a.G - 1);
 
@@ -342,14 +366,15 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a) {
 }
 
 template <int D, int RB, int W, int NS>
-__global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
+__global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   constexpr int KK = D / 32;
   using Ring = KRing<D, W, NS>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g4 = lane >> 4;
-  int g, hg, s;
-  if (!decode_block(a.S2, a.Hkv, a.HG2, g, hg, s)) return;
+  int layer, g, hg, s;
+  if (!decode_block((int)blockIdx.x, a0.S2, a0.Hkv, a0.HG2, a0.layers, layer, g, hg, s)) return;
+  const ScoreArgs a = layer_args(a0, layer);
   const int hl = hg * W + wave;
   const bool active = hl < a.G;
   const int h = g * a.G + min(hl, a.G - 1);
@@ -439,7 +464,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a) {
   for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
   const unsigned ring0 = lds_addr(ring);
   const float invT = 1.f / (float)a.T;
-  const bool direct = (a.agg == SVLM_AGG_QHEAD) || (a.agg == SVLM_AGG_KVHEAD && a.HG2 == 1);
+  const bool direct = !a.layer_mean && ((a.agg == SVLM_AGG_QHEAD) || (a.agg == SVLM_AGG_KVHEAD && a.HG2 == 1));
   // the KV-head mean is taken here when one workgroup holds the whole group, else by score_agg
   const float grp_scale = (direct && a.agg == SVLM_AGG_KVHEAD) ? 1.f / (float)a.G : 1.f;
 
@@ -505,12 +530,8 @@ constexpr int kAggBatch = 16;
 
 // final mean over the group sums (KV-head rows split over several workgroups,
 // or the single all-head row), out = alpha * mean + beta * out
-__global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int r = blockIdx.y;
-  if (i >= a.n_vis) return;
-  int r0, nr;
-  float div;
+// the group-sum rows behind output row r of a layer, and the head count they cover
+__device__ __forceinline__ void group_rows(const ScoreArgs& a, int r, int& r0, int& nr, float& div) {
   if (a.agg == SVLM_AGG_KVHEAD) {
     r0 = r * a.HG2;
     nr = a.HG2;
@@ -520,35 +541,78 @@ __global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
     nr = a.Hkv * a.HG2;
     div = (float)a.Hq;
   }
-  float* o = a.out + (int64_t)r * a.n_vis + i;
-  const float prev = (a.beta == 0.f) ? 0.f : *o;
-  // the group sums are loaded kAggBatch at a time, every load of a batch
-  // issued before the first add (rows past the last are clamped to it and
-  // not added); the adds keep row order
+}
+
+// the sum of group rows r0 .. r0 + nr - 1 at one element (g points at row 0 of
+// the element's column): kAggBatch loads in flight at a time, every load of a
+// batch issued before the first add (rows past the last are clamped to it and
+// not added); the adds keep row order
+__device__ __forceinline__ float sum_group_rows(const float* g, int64_t row_stride, int r0, int nr) {
   float acc = 0.f;
-  const float* g = a.grp + i;
   for (int k0 = 0; k0 < nr; k0 += kAggBatch) {
     float x[kAggBatch];
 #pragma unroll
-    for (int j = 0; j < kAggBatch; ++j) x[j] = g[(int64_t)(r0 + min(k0 + j, nr - 1)) * a.n_vis];
+    for (int j = 0; j < kAggBatch; ++j) x[j] = g[(int64_t)(r0 + min(k0 + j, nr - 1)) * row_stride];
 #pragma unroll
     for (int j = 0; j < kAggBatch; ++j)
       if (k0 + j < nr) acc += x[j];
   }
-  const float v = acc / div;
+  return acc;
+}
+
+// one row set per layer: blockIdx.y = layer * rows + r
+__global__ __launch_bounds__(256) void score_agg(ScoreArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int layer = (int)blockIdx.y / a.rows;
+  const int r = (int)blockIdx.y - layer * a.rows;
+  if (i >= a.n_vis) return;
+  int r0, nr;
+  float div;
+  group_rows(a, r, r0, nr, div);
+  float* o = a.out + (int64_t)blockIdx.y * a.n_vis + i;
+  const float prev = (a.beta == 0.f) ? 0.f : *o;
+  const float v = sum_group_rows(a.grp + layer * a.ws_sl + i, a.n_vis, r0, nr) / div;
   *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * prev;
 }
 
-// (g, s) pairs in groups of 8 (one per XCD), times the head groups
-inline int64_t pass_blocks(int Hkv, int S, int HG) { return ((int64_t)Hkv * S + 7) / 8 * 8 * HG; }
+// the layers averaged into one row set: 64 elements per workgroup, each
+// summed by kAggLanes threads over every kAggLanes-th layer, the lanes then
+// added in a fixed order
+constexpr int kAggLanes = 16;
+__global__ __launch_bounds__(64 * kAggLanes) void score_agg_layers(ScoreArgs a) {
+  const int e = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + e;
+  const int r = blockIdx.y;
+  int r0, nr;
+  float div;
+  group_rows(a, r, r0, nr, div);
+  __shared__ float part[kAggLanes][64];
+  float acc = 0.f;
+  if (i < a.n_vis)
+    for (int l = j; l < a.layers; l += kAggLanes) acc += sum_group_rows(a.grp + l * a.ws_sl + i, a.n_vis, r0, nr);
+  part[j][e] = acc;
+  __syncthreads();
+  if (j != 0 || i >= a.n_vis) return;
+  float tot = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < kAggLanes; ++jj) tot += part[jj][e];
+  const float v = tot / (div * (float)a.layers);
+  float* o = a.out + (int64_t)r * a.n_vis + i;
+  *o = (a.beta == 0.f) ? a.alpha * v : a.alpha * v + a.beta * (*o);
+}
+
+// (layer, g, s) triples in groups of 8 (one per XCD), times the head groups
+inline int64_t pass_blocks(int layers, int Hkv, int S, int HG) {
+  return (mul_sat(mul_sat(layers, Hkv), S) + 7) / 8 * 8 * HG;
+}
 
 template <int D, int RB, int W>
 void launch_pass1(const ScoreArgs& a, hipStream_t st) {
-  score_pass1<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING1>()><<<(unsigned)pass_blocks(a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
+  score_pass1<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING1>()><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
 }
 template <int D, int RB, int W>
 void launch_pass2(const ScoreArgs& a, hipStream_t st) {
-  score_pass2<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING2>()><<<(unsigned)pass_blocks(a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
+  score_pass2<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING2>()><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
 }
 
 template <int D, int RB>
@@ -595,11 +659,21 @@ int pick_waves(int G, int cap) {
   return w;
 }
 
-// key splits so that there is about one workgroup per compute unit, with at
-// least 2 tiles per split; the split length is a whole number of tiles
-int pick_splits(int64_t groups, int64_t keys, int* kps) {
+// key splits: one layer takes about one workgroup per compute unit; several
+// layers in one call take about eight rounds of the chip in all, so each
+// workgroup runs long (its set-up amortised over more tiles) and the last
+// round is a small part of the whole (measured: four rounds are as fast at
+// the 72B and 7B shapes, 2-7% slower at the hour-long one; two rounds 10%
+// slower at the 72B shape).  At least 2 tiles per split; the split length is
+// a whole number of tiles.
+#ifndef SVLM_SCORE_ROUNDS
+#define SVLM_SCORE_ROUNDS 8
+#endif
+int pick_splits(int64_t groups, int64_t keys, int layers, int* kps) {
   const int64_t target = std::max(1, num_cus());
-  int64_t S = std::max<int64_t>(1, (target + groups - 1) / groups);
+  const int64_t many = SVLM_SCORE_ROUNDS * target;  // workgroups of a several-layer call
+  int64_t S = (layers <= 1) ? std::max<int64_t>(1, (target + groups - 1) / groups)
+                            : std::max<int64_t>(1, (many + groups * layers - 1) / (groups * layers));
   const int64_t tiles = (keys + kTileKeys - 1) / kTileKeys;
   S = std::max<int64_t>(1, std::min(S, tiles / 2));
   const int64_t per_tiles = (tiles + S - 1) / S;
@@ -610,16 +684,35 @@ int pick_splits(int64_t groups, int64_t keys, int* kps) {
 struct Geometry {
   int W1, HG1, S1, kps1, W2, HG2, S2, kps2;
 };
-Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis, int layers) {
   Geometry gm;
   const int G = Hq / Hkv;
   gm.W1 = pick_waves(G, 8);
   gm.HG1 = (G + gm.W1 - 1) / gm.W1;
-  gm.S1 = pick_splits((int64_t)Hkv * gm.HG1, (int64_t)q_pos0 + T, &gm.kps1);
+  gm.S1 = pick_splits((int64_t)Hkv * gm.HG1, (int64_t)q_pos0 + T, layers, &gm.kps1);
   gm.W2 = pick_waves(G, 4);
   gm.HG2 = (G + gm.W2 - 1) / gm.W2;
-  gm.S2 = pick_splits((int64_t)Hkv * gm.HG2, n_vis, &gm.kps2);
+  gm.S2 = pick_splits((int64_t)Hkv * gm.HG2, n_vis, layers, &gm.kps2);
   return gm;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// one layer's workspace: the pass-1 row statistics, then the group-sum rows
+struct WsParts {
+  size_t ml, grp, layer;
+};
+WsParts ws_parts(const Geometry& gm, int T, int Hq, int Hkv, int n_vis) {
+  WsParts w;
+  w.ml = align256((size_t)Hq * T * gm.S1 * 2 * sizeof(float));
+  w.grp = (size_t)Hkv * gm.HG2 * n_vis * sizeof(float);
+  w.layer = w.ml + align256(w.grp);
+  return w;
+}
+
+bool ws_sizes_ok(int layers, int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+  return layers >= 1 && T >= 1 && T <= 128 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && q_pos0 >= 0 && n_vis >= 1 &&
+         n_vis <= (1 << 18);
 }
 
 }  // namespace
@@ -627,71 +720,103 @@ Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
 
 using namespace svlm;
 
-extern "C" size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
-  if (T < 1 || T > 128 || Hq < 1 || Hkv < 1 || Hq % Hkv || q_pos0 < 0 || n_vis < 1 || n_vis > (1 << 18)) return 0;
-  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
-  const size_t ml = ((size_t)Hq * T * gm.S1 * 2 * sizeof(float) + 255) / 256 * 256;
-  return ml + (size_t)Hkv * gm.HG2 * n_vis * sizeof(float);
+static size_t score_ws_bytes(int layers, int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+  if (!ws_sizes_ok(layers, T, Hq, Hkv, q_pos0, n_vis)) return 0;
+  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis, layers);
+  // sizes past 2^60 bytes are refused rather than wrapped
+  if (mul_sat(mul_sat(mul_sat(Hq, T), gm.S1), 8) > ((int64_t)1 << 60) ||
+      mul_sat(mul_sat(mul_sat(Hkv, gm.HG2), n_vis), 4) > ((int64_t)1 << 60))
+    return 0;
+  const WsParts w = ws_parts(gm, T, Hq, Hkv, n_vis);
+  // the last layer needs no padding after its rows
+  const size_t last = w.ml + w.grp;
+  if ((size_t)(layers - 1) > (SIZE_MAX - last) / w.layer) return 0;
+  return (size_t)(layers - 1) * w.layer + last;
 }
 
-extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const void* k, int64_t k_sh, int64_t k_sn,
-                          int dtype, int T, int n_ctx, int q_pos0, int vis_start, int n_vis, int Hq, int Hkv, int D,
-                          float scale, int agg, float alpha, float beta, float* out, void* ws, size_t ws_bytes,
-                          void* stream) {
-  if (dtype != SVLM_BF16 && dtype != SVLM_F32) return fail(SVLM_E_UNSUPPORTED, "svlm_score: unknown dtype %d", dtype);
+extern "C" size_t svlm_score_workspace(int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+  return score_ws_bytes(1, T, Hq, Hkv, q_pos0, n_vis);
+}
+
+extern "C" size_t svlm_score_layers_workspace(int layers, int T, int Hq, int Hkv, int q_pos0, int n_vis) {
+  return score_ws_bytes(layers, T, Hq, Hkv, q_pos0, n_vis);
+}
+
+// shared by svlm_score (one layer) and svlm_score_layers
+static int score_impl(const char* name, const void* q_text, int64_t q_st, int64_t q_sh, int64_t q_sl, const void* k,
+                      int64_t k_sh, int64_t k_sn, int64_t k_sl, int layers, int dtype, int T, int n_ctx, int q_pos0,
+                      int vis_start, int n_vis, int Hq, int Hkv, int D, float scale, int agg, int layer_mean,
+                      float alpha, float beta, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != SVLM_BF16 && dtype != SVLM_F32) return fail(SVLM_E_UNSUPPORTED, "%s: unknown dtype %d", name, dtype);
   const int epc = (dtype == SVLM_F32) ? 4 : 8;  // elements per 16 bytes
-  if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "svlm_score: D must be 64 or 128 (got %d)", D);
-  if (T < 1 || T > 128) return fail(SVLM_E_UNSUPPORTED, "svlm_score: 1 <= T <= 128 text queries supported (got %d)", T);
-  if (!q_text || !k || !out) return fail(SVLM_E_INVALID, "svlm_score: null pointer");
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(SVLM_E_INVALID, "svlm_score: Hq must be a positive multiple of Hkv");
+  if (D != 64 && D != 128) return fail(SVLM_E_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", name, D);
+  if (T < 1 || T > 128) return fail(SVLM_E_UNSUPPORTED, "%s: 1 <= T <= 128 text queries supported (got %d)", name, T);
+  if (layers < 1) return fail(SVLM_E_INVALID, "%s: layers must be >= 1", name);
+  if (!q_text || !k || !out) return fail(SVLM_E_INVALID, "%s: null pointer", name);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(SVLM_E_INVALID, "%s: Hq must be a positive multiple of Hkv", name);
   if (n_ctx < 1 || q_pos0 < 0 || (int64_t)q_pos0 + T > n_ctx)
-    return fail(SVLM_E_INVALID, "svlm_score: need 0 <= q_pos0 and q_pos0 + T <= n_ctx");
+    return fail(SVLM_E_INVALID, "%s: need 0 <= q_pos0 and q_pos0 + T <= n_ctx", name);
   if (n_vis < 1 || n_vis > (1 << 18) || vis_start < 0 || (int64_t)vis_start + n_vis > (int64_t)q_pos0 + 1)
-    return fail(SVLM_E_INVALID, "svlm_score: visual range must lie in [0, q_pos0] (every text query sees it)");
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVLM_E_INVALID, "svlm_score: scale must be finite and > 0");
+    return fail(SVLM_E_INVALID, "%s: visual range must lie in [0, q_pos0] (every text query sees it)", name);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SVLM_E_INVALID, "%s: scale must be finite and > 0", name);
   if (agg != SVLM_AGG_QHEAD && agg != SVLM_AGG_KVHEAD && agg != SVLM_AGG_ALL)
-    return fail(SVLM_E_INVALID, "svlm_score: unknown aggregation %d", agg);
-  if (!std::isfinite(alpha) || !std::isfinite(beta)) return fail(SVLM_E_INVALID, "svlm_score: alpha, beta must be finite");
-  if (!aligned16(q_text) || !aligned16(k)) return fail(SVLM_E_INVALID, "svlm_score: q_text and k must be 16-byte aligned");
-  if (q_st % epc || q_sh % epc || k_sh % epc || k_sn % epc || k_sn < D || q_st < 0 || q_sh < 0 || k_sh < 0)
-    return fail(SVLM_E_INVALID, "svlm_score: strides must be non-negative multiples of 16 bytes, k_sn >= D");
+    return fail(SVLM_E_INVALID, "%s: unknown aggregation %d", name, agg);
+  if (layer_mean != 0 && layer_mean != 1) return fail(SVLM_E_INVALID, "%s: layer_mean must be 0 or 1", name);
+  if (layers == 1) layer_mean = 0;  // the mean of one layer is that layer
+  if (layer_mean && agg == SVLM_AGG_QHEAD)
+    return fail(SVLM_E_UNSUPPORTED, "%s: the layer mean takes SVLM_AGG_KVHEAD or SVLM_AGG_ALL", name);
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return fail(SVLM_E_INVALID, "%s: alpha, beta must be finite", name);
+  if (!aligned16(q_text) || !aligned16(k)) return fail(SVLM_E_INVALID, "%s: q_text and k must be 16-byte aligned", name);
+  if (q_st % epc || q_sh % epc || k_sh % epc || k_sn % epc || q_sl % epc || k_sl % epc || k_sn < D || q_st < 0 ||
+      q_sh < 0 || k_sh < 0 || q_sl < 0 || k_sl < 0)
+    return fail(SVLM_E_INVALID, "%s: strides must be non-negative multiples of 16 bytes, k_sn >= D", name);
   const int out_rows = (agg == SVLM_AGG_QHEAD) ? Hq : (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
-  if (dtype == SVLM_F32) {
-    // plain fp32 path: row log-sum-exp into the workspace, then the
-    // aggregated column means straight into out
-    if (!grid_fits((int64_t)Hq * T, 64) || !grid_fits((n_vis + 255) / 256, 256, out_rows))
-      return fail(SVLM_E_UNSUPPORTED, "svlm_score: %d heads exceed the launch limit", Hq);
-    const size_t need = svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis);
+  // the workspace check, after the launch-limit checks of each path
+  auto ws_check = [&]() -> int {
+    const size_t need = score_ws_bytes(layers, T, Hq, Hkv, q_pos0, n_vis);
+    if (need == 0) return fail(SVLM_E_UNSUPPORTED, "%s: the workspace size overflows", name);
     if (!ws || ws_bytes < need)
-      return fail(SVLM_E_WORKSPACE, "svlm_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-    if (!aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_score: workspace must be 16-byte aligned");
-    ScoreF32Args f;
-    f.q = (const float*)q_text;
-    f.q_st = q_st;
-    f.q_sh = q_sh;
-    f.k = (const float*)k;
-    f.k_sh = k_sh;
-    f.k_sn = k_sn;
-    f.T = T;
-    f.q_pos0 = q_pos0;
-    f.vis_start = vis_start;
-    f.n_vis = n_vis;
-    f.Hq = Hq;
-    f.Hkv = Hkv;
-    f.D = D;
-    f.scale = scale;
-    f.lse = (float*)ws;
-    f.agg = agg;
-    f.alpha = alpha;
-    f.beta = beta;
-    f.out = out;
-    launch_score_f32(f, out_rows, (hipStream_t)stream);
-    return check_launch("svlm_score");
+      return fail(SVLM_E_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(SVLM_E_INVALID, "%s: workspace must be 16-byte aligned", name);
+    return SVLM_OK;
+  };
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == SVLM_F32) {
+    // plain fp32 path, one layer at a time: row log-sum-exp into the
+    // workspace, then the aggregated column means straight into out (the
+    // layer mean accumulates through alpha / beta)
+    if (!grid_fits((int64_t)Hq * T, 64) || !grid_fits((n_vis + 255) / 256, 256, out_rows))
+      return fail(SVLM_E_UNSUPPORTED, "%s: %d heads exceed the launch limit", name, Hq);
+    if (const int e = ws_check()) return e;
+    for (int l = 0; l < layers; ++l) {
+      ScoreF32Args f;
+      f.q = (const float*)q_text + l * q_sl;
+      f.q_st = q_st;
+      f.q_sh = q_sh;
+      f.k = (const float*)k + l * k_sl;
+      f.k_sh = k_sh;
+      f.k_sn = k_sn;
+      f.T = T;
+      f.q_pos0 = q_pos0;
+      f.vis_start = vis_start;
+      f.n_vis = n_vis;
+      f.Hq = Hq;
+      f.Hkv = Hkv;
+      f.D = D;
+      f.scale = scale;
+      f.lse = (float*)ws;
+      f.agg = agg;
+      f.alpha = layer_mean ? alpha / (float)layers : alpha;
+      f.beta = (layer_mean && l > 0) ? 1.f : beta;
+      f.out = out + (layer_mean ? 0 : (int64_t)l * out_rows * n_vis);
+      launch_score_f32(f, out_rows, st);
+    }
+    return check_launch(name);
   }
   // buffer-descriptor ranges and offsets are 32-bit: one head's text queries,
   // and one KV head's keys (plus the tiles staged past a split's end)
   if (((int64_t)(T - 1) * q_st + D) * 2 > INT32_MAX || ((int64_t)n_ctx + 1024) * k_sn * 2 > INT32_MAX)
-    return fail(SVLM_E_UNSUPPORTED, "svlm_score: (T-1) * q_st + D and (n_ctx + 1024) * k_sn must stay below 2^30 elements");
+    return fail(SVLM_E_UNSUPPORTED, "%s: (T-1) * q_st + D and (n_ctx + 1024) * k_sn must stay below 2^30 elements", name);
   ScoreArgs a;
   a.q = (const uint16_t*)q_text;
   a.q_st = q_st;
@@ -709,35 +834,57 @@ extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const 
   a.G = Hq / Hkv;
   a.c = scale * kLog2e;
   // pass 1 covers keys [0, q_pos0 + T): everything any text row sees
-  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis);
-  if (!grid_fits(pass_blocks(Hkv, gm.S1, gm.HG1), 64 * gm.W1) || !grid_fits(pass_blocks(Hkv, gm.S2, gm.HG2), 64 * gm.W2) ||
-      !grid_fits((n_vis + 255) / 256, 256, out_rows))
-    return fail(SVLM_E_UNSUPPORTED, "svlm_score: %d heads exceed the launch limit", Hq);
+  const Geometry gm = geometry(T, Hq, Hkv, q_pos0, n_vis, layers);
+  const int64_t blocks1 = pass_blocks(layers, Hkv, gm.S1, gm.HG1), blocks2 = pass_blocks(layers, Hkv, gm.S2, gm.HG2);
+  const bool direct = !layer_mean && ((agg == SVLM_AGG_QHEAD) || (agg == SVLM_AGG_KVHEAD && gm.HG2 == 1));
+  if (!grid_fits(blocks1, 64 * gm.W1) || !grid_fits(blocks2, 64 * gm.W2) ||
+      !grid_fits((n_vis + 255) / 256, 256, mul_sat(layers, out_rows)) || blocks1 > INT32_MAX || blocks2 > INT32_MAX)
+    return fail(SVLM_E_UNSUPPORTED, "%s: %d layers of %d heads exceed the launch limit", name, layers, Hq);
+  if (const int e = ws_check()) return e;
   a.HG1 = gm.HG1;
   a.HG2 = gm.HG2;
   a.S1 = gm.S1;
   a.kps1 = gm.kps1;
   a.S2 = gm.S2;
   a.kps2 = gm.kps2;
-  const size_t ml_bytes = ((size_t)Hq * T * a.S1 * 2 * sizeof(float) + 255) / 256 * 256;
-  const size_t need = svlm_score_workspace(T, Hq, Hkv, q_pos0, n_vis);
-  if (!ws || ws_bytes < need)
-    return fail(SVLM_E_WORKSPACE, "svlm_score: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (!aligned16(ws)) return fail(SVLM_E_INVALID, "svlm_score: workspace must be 16-byte aligned");
+  const WsParts w = ws_parts(gm, T, Hq, Hkv, n_vis);
   a.ml = (float*)ws;
-  a.grp = (float*)((char*)ws + ml_bytes);
+  a.grp = (float*)((char*)ws + w.ml);
   a.agg = agg;
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
-  hipStream_t st = (hipStream_t)stream;
+  a.layers = layers;
+  a.q_sl = q_sl;
+  a.k_sl = k_sl;
+  a.ws_sl = (int64_t)(w.layer / sizeof(float));
+  a.layer_mean = layer_mean;
+  a.rows = out_rows;
   const int rb = pick_rb(T);
   if (D == 128) launch_d<128>(a, rb, gm.W1, gm.W2, st);
   else launch_d<64>(a, rb, gm.W1, gm.W2, st);
-  const bool direct = (agg == SVLM_AGG_QHEAD) || (agg == SVLM_AGG_KVHEAD && gm.HG2 == 1);
-  if (!direct) {
-    const int rows = (agg == SVLM_AGG_KVHEAD) ? Hkv : 1;
-    score_agg<<<dim3((unsigned)((n_vis + 255) / 256), (unsigned)rows), 256, 0, st>>>(a);
+  if (layer_mean) {
+    score_agg_layers<<<dim3((unsigned)((n_vis + 63) / 64), (unsigned)out_rows), 64 * kAggLanes, 0, st>>>(a);
+  } else if (!direct) {
+    score_agg<<<dim3((unsigned)((n_vis + 255) / 256), (unsigned)(layers * out_rows)), 256, 0, st>>>(a);
   }
-  return check_launch("svlm_score");
+  return check_launch(name);
+}
+
+extern "C" int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh, const void* k, int64_t k_sh, int64_t k_sn,
+                          int dtype, int T, int n_ctx, int q_pos0, int vis_start, int n_vis, int Hq, int Hkv, int D,
+                          float scale, int agg, float alpha, float beta, float* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return score_impl("svlm_score", q_text, q_st, q_sh, 0, k, k_sh, k_sn, 0, 1, dtype, T, n_ctx, q_pos0, vis_start,
+                    n_vis, Hq, Hkv, D, scale, agg, 0, alpha, beta, out, ws, ws_bytes, stream);
+}
+
+extern "C" int svlm_score_layers(const void* q_text, int64_t q_st, int64_t q_sh, int64_t q_sl, const void* k,
+                                 int64_t k_sh, int64_t k_sn, int64_t k_sl, int layers, int dtype, int T, int n_ctx,
+                                 int q_pos0, int vis_start, int n_vis, int Hq, int Hkv, int D, float scale, int agg,
+                                 int layer_mean, float alpha, float beta, float* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return score_impl("svlm_score_layers", q_text, q_st, q_sh, q_sl, k, k_sh, k_sn, k_sl, layers, dtype, T, n_ctx,
+                    q_pos0, vis_start, n_vis, Hq, Hkv, D, scale, agg, layer_mean, alpha, beta, out, ws, ws_bytes,
+                    stream);
 }

@@ -101,6 +101,45 @@ def score(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_st
     return out
 
 
+def score_layers_workspace_bytes(layers: int, T: int, Hq: int, Hkv: int, q_pos0: int, n_vis: int) -> int:
+    return int(L.load().svlm_score_layers_workspace(layers, T, Hq, Hkv, q_pos0, n_vis))
+
+
+def score_layers(q_text: torch.Tensor, k: torch.Tensor, q_pos0: int, n_vis: int, vis_start: int = 0,
+                 agg: str = "all", layer_mean: bool = True, alpha: float = 1.0, beta: float = 0.0,
+                 out: torch.Tensor | None = None, scale: float | None = None,
+                 ws: torch.Tensor | None = None) -> torch.Tensor:
+    """score() over every layer in one call.  q_text [L][T][Hq][D], k [L][Hkv][n_ctx][D].
+    layer_mean: out [rows][n_vis] = the mean over layers of each layer's rows;
+    otherwise out [L][rows][n_vis], one row set per layer."""
+    _dev(q_text, k, out, ws)
+    dtype = _operands(q_text, k)
+    if q_text.dim() != 4 or k.dim() != 4 or q_text.shape[0] != k.shape[0]:
+        raise ValueError("q_text must be [L][T][Hq][D] and k [L][Hkv][n_ctx][D] with the same L")
+    layers, T, Hq, D = q_text.shape
+    _, Hkv, n_ctx, Dk = k.shape
+    if Dk != D:
+        raise ValueError("head dims differ")
+    rows = {"qhead": Hq, "kvhead": Hkv, "all": 1}[agg]
+    shape = (rows, n_vis) if layer_mean else (layers, rows, n_vis)
+    if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing out")
+        out = torch.empty(shape, dtype=torch.float32, device=q_text.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
+        raise ValueError(f"out must be contiguous fp32 {list(shape)}")
+    need = score_layers_workspace_bytes(layers, T, Hq, Hkv, q_pos0, n_vis)
+    if ws is None:
+        ws = _ws(need, q_text.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    L.call("svlm_score_layers", q_text.data_ptr(), q_text.stride(1), q_text.stride(2), q_text.stride(0),
+           k.data_ptr(), k.stride(1), k.stride(2), k.stride(0), layers, dtype, T, n_ctx, q_pos0, vis_start, n_vis,
+           Hq, Hkv, D, float(scale), _AGG[agg], int(bool(layer_mean)), float(alpha), float(beta), out.data_ptr(),
+           ws.data_ptr(), _nbytes(ws), _stream())
+    return out
+
+
 # ---------------------------------------------------------------------------
 def select_workspace_bytes(R: int, n_vis: int, budget: int, top_p: float) -> int:
     return int(L.load().svlm_select_workspace(R, n_vis, budget, float(top_p)))

@@ -632,7 +632,25 @@ def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
     out["verify_attn"]["what"] = "dense verify, 10 queries x 141194 keys, 28 q / 4 KV heads, D 128"
     out["draft_attn_indexed"]["what"] = ("draft, 1 query over per-head lists of 1024 visual + 64 text + 1 rows "
                                          "read in place")
-    del kv
+    del kv, qv, qd
+    torch.cuda.empty_cache()
+    # the selection rows themselves: the score of all 28 layers in one call,
+    # one row per (layer, KV head), over 141120 visual + 64 text keys
+    T, NV, L = c5.n_text, c5.n_vis, c5.layers
+    k = torch.empty(L, Hkv, NV + T, D, dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        k[l].copy_(torch.randn(Hkv, NV + T, D, generator=g, device=dev, dtype=torch.float32))
+    qt = torch.randn(L, T, Hq, D, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ws_s = torch.empty(ops.score_layers_workspace_bytes(L, T, Hq, Hkv, NV, NV), dtype=torch.uint8, device=dev)
+    rows = ops.score_layers(qt, k, NV, NV, agg="kvhead", layer_mean=False, ws=ws_s)
+    us = graph_us(torch, lambda: ops.score_layers(qt, k, NV, NV, agg="kvhead", layer_mean=False, out=rows, ws=ws_s),
+                  L, max(2, steps // 2))
+    flop = 2 * D * Hq * (T * NV + T * (T + 1) // 2) + 2 * D * Hq * T * NV
+    out["score"] = {"us_avg": round(us, 3), "flop": flop, "tflops": round(flop / (us * 1e-6) / 1e12, 1),
+                    "frac_bf16_peak": round(flop / (us * 1e-6) / 1e12 / 2500.0, 4),
+                    "what": "per layer: the 28 layers' score in one call, one row per (layer, KV head) = the 112 "
+                            "rows the selection takes"}
+    del k, qt, ws_s, rows
     return out
 
 

@@ -341,3 +341,22 @@ def test_llava72b_eighty_layers_equal_per_layer_calls():
     rel = float((np.abs(a - b) / np.abs(b)).max())
     log(f"  max relative difference {rel:.2e}")
     assert rel <= 1e-5
+
+
+def test_hour_long_two_layers_in_one_call_sampled_kv_heads():
+    """Two hour-long layers (141120 visual + 64 text tokens, 28 q / 4 KV heads)
+    in one call with one row per (layer, KV head), the rows the hour-long
+    top-K consumes; the oracle checks KV heads 0 and 3 of both layers."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C5
+    ps, q, k = _stack_layers(cfg, 2)
+    log("score_layers case hour-long x2, per (layer, KV head)")
+    out = ops.score_layers(dev_bf16(q), dev_bf16(k), ps[0].q_pos0, cfg.n_vis, agg="kvhead", layer_mean=False)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    G = cfg.group
+    for l, p in enumerate(ps):
+        for g in (0, cfg.hkv - 1):
+            heads = list(range(g * G, (g + 1) * G))
+            sq = oracle.score_layer(p.q_text[:, heads], p.k[g:g + 1], p.q_pos0, 0, cfg.n_vis, 1)
+            _compare(got[l, g:g + 1], oracle.aggregate_heads(sq, 1, "kvhead"), f"hour-long layer {l} kv head {g}")

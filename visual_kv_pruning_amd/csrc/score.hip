@@ -16,12 +16,13 @@
 // the KV group (up to 8).  The key tile (64 keys) is staged HBM -> LDS once by
 // LDS-DMA transfers that all waves share (one barrier per tile), so K is read
 // from memory once per workgroup; the text queries of a wave's head sit in
-// registers.  Both passes use v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
-// pass 1 computes S^T (lane = one text row x 4 keys per 16-key block) and keeps
-// a lazily raised reference maximum per lane group, so a key costs one fma,
-// one exp2 and one add; pass 2 computes S (lane = 4 text rows x one key), so a
-// column sum over the rows needs two cross-lane steps per tile, and the waves
-// add their heads through LDS.  Exp throughput bounds both passes.
+// registers.  Both passes use v_mfma_f32_16x16x32_bf16 with fp32 accumulation
+// and compute S^T (lane = one text row x 4 keys per 16-key block, so a lane
+// needs one log-sum-exp per row block).  Pass 1 keeps a lazily raised
+// reference maximum per lane group, so a key costs one fma, one exp2 and one
+// add; pass 2 adds a lane's row blocks in registers and the 16 row lanes of
+// each key through LDS, and the waves add their heads through LDS.  Several
+// layers can share one launch of each pass.
 #include <cmath>
 
 #include "svlm_internal.h"
@@ -156,6 +157,14 @@ struct KRing {
       src_lane[i] = r * row_bytes + ((p ^ (r % CH)) * 16);
     }
   }
+  __device__ void stage_to(unsigned char* dst, int tile) const {
+    const int soff = tile * kTileKeys * row_bytes;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (wave * PW + i) * 1024), 16, src_lane[i],
+          soff, 0, kNT);
+  }
   __device__ void stage(int slot, int tile) const {
     const int soff = tile * kTileKeys * row_bytes;
 #pragma unroll
@@ -167,36 +176,6 @@ struct KRing {
   // LDS byte offset (within a slot) of the lane's K operand chunk: key row r, d chunk kk*4 + g4
   static __device__ unsigned koff(int r, int kk, int g4) { return r * ROWB + (((kk * 4 + g4) ^ (r % CH)) * 16); }
 };
-
-// the lane's part of the column sum of P = exp2(c s - lse) for one 16-key
-// block (lane: rows 16 rb + 4 g4 + i, key c).  One block at a time keeps the
-// score accumulators few enough to live in ordinary VGPRs next to the query
-// registers, so the exponentials read them without accumulator moves.
-template <int RB, int KK>
-__device__ __forceinline__ float qk_colsum_block(const u32x4 (&q)[RB][KK], const u32x4 (&kq)[KK],
-                                                 const float (&lse)[RB][4], float c) {
-  f32x4 S[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) S[rb] = mfma16(as_bf16x8(q[rb][kk]), as_bf16x8(kq[kk]), S[rb]);
-  }
-  // pairwise sums (a fixed tree, not one serial chain of RB * 4 dependent adds)
-  float r[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(S[rb][i], c, -lse[rb][i]));
-    r[rb] = (e[0] + e[1]) + (e[2] + e[3]);
-  }
-#pragma unroll
-  for (int w = 1; w < RB; w *= 2)
-#pragma unroll
-    for (int rb = 0; rb + w < RB; rb += 2 * w) r[rb] += r[rb + w];
-  return r[0];
-}
 
 // the 2 * KK K-operand chunks of key blocks kb0, kb0 + 1 of a staged tile
 template <int KK, int BLOCK_BYTES>
@@ -249,7 +228,10 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   int layer, g, hg, s;
   if (!decode_block((int)blockIdx.x, a0.S1, a0.Hkv, a0.HG1, a0.layers, layer, g, hg, s)) return;
   const ScoreArgs a = layer_args(a0, layer);
-  const int hl = hg * W + wave;  // head within the KV group; waves past the group compute but do not write
+  const int hl = hg * W + wave;  // head within the KV group
+  // waves past the group (W rounds G up to a power of two) stage their share
+  // of every K tile and meet every barrier, but skip the arithmetic
+  const bool active = hl < a.G;
   const int h = g * a.G + min(hl, a.G - 1);
 
   const int k_begin = s * a.kps1;
@@ -287,6 +269,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
     wait_vmcnt<(NS - 2) * Ring::PW>();  // this wave's share of tile t has landed
     wg_barrier();                       // every share of tile t has landed; tile t-1 is retired
     kr.stage((t + NS - 1) % NS, t + NS - 1);
+    if (!active) return;
     const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
     u32x4 kq2[2][KK];  // K operands of two blocks per LDS wait
 #pragma unroll
@@ -360,7 +343,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
       ll = l0;
     }
     const int tq = rb * 16 + c;
-    if (g4 == 0 && hl < a.G && tq < a.T)
+    if (g4 == 0 && active && tq < a.T)
       *(float2*)(a.ml + (((int64_t)h * a.S1 + s) * a.T + tq) * 2) = make_float2(m, ll);
   }
 }
@@ -383,9 +366,13 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   const int v_end = min(v_begin + a.kps2, a.vis_start + a.n_vis);
   const int n_tiles = (v_end > v_begin) ? (v_end - v_begin + kTileKeys - 1) / kTileKeys : 0;
 
-  __shared__ __align__(16) unsigned char ring[NS * Ring::TB];
+  static_assert(NS == 3, "three named staging slots");
+  __shared__ __align__(16) unsigned char ring[Ring::TB];
+  __shared__ __align__(16) unsigned char ring_b[Ring::TB];
+  __shared__ __align__(16) unsigned char ring_c[Ring::TB];
   __shared__ float sm_lse[W][RB * 16];
   __shared__ float xch[2][W][kTileKeys];
+  __shared__ __align__(16) float red[W][kTileKeys][20];
   Ring kr;
   kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)v_begin * a.k_sn, max(v_end - v_begin, 0), a.k_sn, ring, wave);
 
@@ -435,8 +422,8 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   {
     float2 part[RPL][kLseBatch];
     load_parts(0, part);
-#pragma unroll
-    for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
+    kr.stage_to(ring, 0);
+    kr.stage_to(ring_b, 1);
     merge_parts(part);
   }
   for (int s0 = kLseBatch; s0 < a.S1; s0 += kLseBatch) {
@@ -453,16 +440,13 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   u32x4 qreg[RB][KK];
   load_q<D, RB>(a, h, qreg);
   wait_lgkmcnt0();
-  float lse[RB][4];  // rows 16 rb + 4 g4 + i
+  float lse_t[RB];  // the lane's text rows 16 rb + c
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lse[rb][i] = sm_lse[wave][rb * 16 + 4 * g4 + i];
+  for (int rb = 0; rb < RB; ++rb) lse_t[rb] = sm_lse[wave][rb * 16 + c];
 
   unsigned ko[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
-  const unsigned ring0 = lds_addr(ring);
   const float invT = 1.f / (float)a.T;
   const bool direct = !a.layer_mean && ((a.agg == SVLM_AGG_QHEAD) || (a.agg == SVLM_AGG_KVHEAD && a.HG2 == 1));
   // the KV-head mean is taken here when one workgroup holds the whole group, else by score_agg
@@ -489,35 +473,62 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
     if (key < v_end) emit(direct ? g : g * a.HG2 + hg, key, v * grp_scale);
   };
 
-  // (the compiler waits for the query loads before their first use; tile t's
-  // wait below also covers the loads issued after it)
-  for (int t = 0; t < n_tiles; ++t) {
+  auto body = [&](int t, const unsigned char* rd, unsigned char* dma) __attribute__((always_inline)) {
     wait_vmcnt<(NS - 2) * Ring::PW>();
     wait_lgkmcnt0();  // this wave's column means of tile t-1 are in LDS
     wg_barrier();
-    kr.stage((t + NS - 1) % NS, t + NS - 1);
+    kr.stage_to(dma, t + NS - 1);
     if (a.agg != SVLM_AGG_QHEAD && t > 0) flush(t - 1);
-    const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
-    float col[4];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {  // K operands of two blocks per LDS wait
-      u32x4 kq2[2][KK];
-      read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(kp * 32 * Ring::ROWB), ko, kq2);
-      col[2 * kp] = qk_colsum_block<RB, KK>(qreg, kq2[0], lse, a.c);
-      col[2 * kp + 1] = qk_colsum_block<RB, KK>(qreg, kq2[1], lse, a.c);
+    const int key = v_begin + t * kTileKeys + lane;
+    if (!active) {  // waves past the group add nothing
+      if (a.agg != SVLM_AGG_QHEAD) xch[t & 1][wave][lane] = 0.f;
+      return;
     }
-    // column sums over the rows held by the four lane groups; lane (c, g4) then
-    // keeps key 16 g4 + c of the tile
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) col[kb] = sum_xor32(sum_xor16(col[kb]));
-    const float v = ((g4 == 0) ? col[0] : (g4 == 1) ? col[1] : (g4 == 2) ? col[2] : col[3]) * invT;
-    const int key = v_begin + t * kTileKeys + 16 * g4 + c;
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4 kq[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kq[kk] = *(const u32x4*)(rd + kb * 16 * Ring::ROWB + ko[kk]);
+      f32x4 S[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) S[rb] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), S[rb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) e[rb] = fast_exp2(fmaf(S[rb][i], a.c, -lse_t[rb]));
+#pragma unroll
+        for (int w2 = 1; w2 < RB; w2 *= 2)
+#pragma unroll
+          for (int rb = 0; rb + w2 < RB; rb += 2 * w2) e[rb] += e[rb + w2];
+        red[wave][16 * kb + 4 * g4 + i][c] = e[0];
+      }
+    }
+    float4 rr[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) rr[q4] = *(const float4*)&red[wave][lane][4 * q4];
+    float v = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) v = (((v + rr[q4].x) + rr[q4].y) + rr[q4].z) + rr[q4].w;
+    v *= invT;
     if (a.agg == SVLM_AGG_QHEAD) {
       if (active && key < v_end) emit(h, key, v);
     } else {
-      xch[t & 1][wave][16 * g4 + c] = active ? v : 0.f;
+      xch[t & 1][wave][lane] = active ? v : 0.f;
     }
+  };
+  int t = 0;
+  for (; t + 3 <= n_tiles; t += 3) {
+    body(t, ring, ring_c);
+    body(t + 1, ring_b, ring);
+    body(t + 2, ring_c, ring_b);
   }
+  if (t < n_tiles) body(t, ring, ring_c);
+  if (t + 1 < n_tiles) body(t + 1, ring_b, ring);
   wait_vmcnt<0>();
   if (a.agg != SVLM_AGG_QHEAD && n_tiles > 0) {
     wait_lgkmcnt0();
@@ -626,7 +637,8 @@ void launch_rb(const ScoreArgs& a, int w1, int w2, hipStream_t st) {
   switch (w2) {
     case 1: launch_pass2<D, RB, 1>(a, st); break;
     case 2: launch_pass2<D, RB, 2>(a, st); break;
-    default: launch_pass2<D, RB, 4>(a, st); break;
+    case 4: launch_pass2<D, RB, 4>(a, st); break;
+    default: launch_pass2<D, RB, 8>(a, st); break;
   }
 }
 
@@ -651,8 +663,13 @@ int pick_rb(int T) {
 
 // waves per workgroup: the q heads of a KV group, rounded up to a power of two,
 // at most `cap`.  Pass 1 takes up to 8 (two waves per SIMD hide each other's
-// waits); pass 2 up to 4 (it is bound by exp throughput, and one wave per SIMD
-// spares the barrier across eight)
+// waits).  Pass 2 takes up to 8 on visual ranges of at least kPass2WideKeys
+// keys, up to 4 on shorter ones: eight waves hold one head group per
+// workgroup (half the workgroups, each over more keys), which pays on long
+// rows and loses on short ones, where the per-wave set-up dominates
+// (measured: 72B 96-99 against 100-104 us per layer, 32B 56 against 61,
+// hour-long 153 against 157; 7B, 8192 keys, 13.8 against 12.0)
+constexpr int kPass2WideKeys = 16384;
 int pick_waves(int G, int cap) {
   int w = 1;
   while (w < G && w < cap) w *= 2;
@@ -690,7 +707,7 @@ Geometry geometry(int T, int Hq, int Hkv, int q_pos0, int n_vis, int layers) {
   gm.W1 = pick_waves(G, 8);
   gm.HG1 = (G + gm.W1 - 1) / gm.W1;
   gm.S1 = pick_splits((int64_t)Hkv * gm.HG1, (int64_t)q_pos0 + T, layers, &gm.kps1);
-  gm.W2 = pick_waves(G, 4);
+  gm.W2 = pick_waves(G, n_vis >= kPass2WideKeys ? 8 : 4);
   gm.HG2 = (G + gm.W2 - 1) / gm.W2;
   gm.S2 = pick_splits((int64_t)Hkv * gm.HG2, n_vis, layers, &gm.kps2);
   return gm;

@@ -360,3 +360,21 @@ def test_hour_long_two_layers_in_one_call_sampled_kv_heads():
             heads = list(range(g * G, (g + 1) * G))
             sq = oracle.score_layer(p.q_text[:, heads], p.k[g:g + 1], p.q_pos0, 0, cfg.n_vis, 1)
             _compare(got[l, g:g + 1], oracle.aggregate_heads(sq, 1, "kvhead"), f"hour-long layer {l} kv head {g}")
+
+
+@pytest.mark.parametrize("rows", ["all", "layer_kvhead"])
+def test_layers_fp32_operands(rows):
+    """svlm_score_layers on fp32 operands (the plain fp32 kernels, one layer
+    after another): three unrounded tiny-shape layers against the oracle."""
+    from visual_kv_pruning_amd import ops
+    cfg = W.C1
+    ps = [W.prefill_layer(cfg, l, round_bf16=False) for l in range(3)]
+    q = np.stack([p.q_text for p in ps])
+    k = np.stack([p.k for p in ps])
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+    agg, mean = ("all", True) if rows == "all" else ("kvhead", False)
+    log(f"score_layers case tiny fp32 x3 {rows}")
+    out = ops.score_layers(f32(q), f32(k), ps[0].q_pos0, cfg.n_vis, agg=agg, layer_mean=mean)
+    torch.cuda.synchronize()
+    ref = oracle.score_rows_for_config([(p.q_text, p.k) for p in ps], ps[0].q_pos0, cfg.n_vis, cfg.hkv, rows)
+    _compare(out.cpu().numpy().reshape(-1, cfg.n_vis), ref, f"tiny fp32 x3 {rows}", rel_tol=F32_REL_TOL)

@@ -143,9 +143,10 @@ int svlm_score(const void* q_text, int64_t q_st, int64_t q_sh,
  *                   [layers][rows][n_vis].
  * With layers == 1 it is svlm_score (bit for bit, either layer_mean).
  * The layers share the launches: the key splits are planned over all of
- * them (about four rounds of workgroups over the chip), so each workgroup
- * covers more keys than in a one-layer call and the results differ from
- * per-layer svlm_score calls by fp32 reordering only.
+ * them (at least four rounds of workgroups over the chip, whole rounds
+ * preferred), so each workgroup covers more keys than in a one-layer call
+ * and the results differ from per-layer svlm_score calls by fp32
+ * reordering only.
  * ws: svlm_score_layers_workspace(layers, T, Hq, Hkv, q_pos0, n_vis) bytes
  *     (the per-layer statistics and group rows of every layer).
  * Errors as svlm_score; layers < 1 or layer_mean outside {0, 1} is

@@ -676,23 +676,47 @@ int pick_waves(int G, int cap) {
   return w;
 }
 
-// key splits: one layer takes about one workgroup per compute unit; several
-// layers in one call take about eight rounds of the chip in all, so each
-// workgroup runs long (its set-up amortised over more tiles) and the last
-// round is a small part of the whole (measured: four rounds are as fast at
-// the 72B and 7B shapes, 2-7% slower at the hour-long one; two rounds 10%
-// slower at the 72B shape).  At least 2 tiles per split; the split length is
-// a whole number of tiles.
+// key splits: one layer takes about one workgroup per compute unit.  Several
+// layers in one call take at least SVLM_SCORE_ROUNDS rounds of workgroups
+// over the chip (one per CU); among up to four times that many splits, the
+// count whose (rounds) x (set-up + tiles per workgroup) is least, which
+// prefers long workgroups (set-up paid over more tiles) and whole rounds (no
+// idle tail).  Measured against a fixed eight rounds, µs per layer: 72B 94.4
+// against 96.1-97.2, 32B 54.8 against 56.2, 7B 11.1 against 12.4-13.3,
+// hour-long 142-144 against 153-154.  At least 2 tiles per split; the split
+// length is a whole number of tiles.
 #ifndef SVLM_SCORE_ROUNDS
-#define SVLM_SCORE_ROUNDS 8
+#define SVLM_SCORE_ROUNDS 4
 #endif
+constexpr int64_t kSetupTiles = 4;
 int pick_splits(int64_t groups, int64_t keys, int layers, int* kps) {
   const int64_t target = std::max(1, num_cus());
-  const int64_t many = SVLM_SCORE_ROUNDS * target;  // workgroups of a several-layer call
-  int64_t S = (layers <= 1) ? std::max<int64_t>(1, (target + groups - 1) / groups)
-                            : std::max<int64_t>(1, (many + groups * layers - 1) / (groups * layers));
   const int64_t tiles = (keys + kTileKeys - 1) / kTileKeys;
-  S = std::max<int64_t>(1, std::min(S, tiles / 2));
+  const int64_t smax = std::max<int64_t>(1, tiles / 2);
+  int64_t S;
+  if (layers <= 1) {
+    S = std::max<int64_t>(1, (target + groups - 1) / groups);
+  } else {
+    // at least SVLM_SCORE_ROUNDS rounds of workgroups; within four times that
+    // many splits, the count that minimises (rounds) x (set-up + tiles per
+    // workgroup), the set-up counted as kSetupTiles tiles
+    const int64_t units = mul_sat(groups, layers);
+    const int64_t need = SVLM_SCORE_ROUNDS * target;
+    const int64_t lo = std::min(smax, (units >= need) ? (int64_t)1 : (need + units - 1) / units);
+    const int64_t hi = std::min(smax, 4 * lo);
+    int64_t best_cost = INT64_MAX;
+    S = lo;
+    for (int64_t s = lo; s <= hi; ++s) {
+      const int64_t n = mul_sat(units, s);
+      const int64_t rounds = n / target + (n % target != 0);
+      const int64_t cost = mul_sat(rounds, kSetupTiles + (tiles + s - 1) / s);
+      if (cost < best_cost) {
+        best_cost = cost;
+        S = s;
+      }
+    }
+  }
+  S = std::max<int64_t>(1, std::min(S, smax));
   const int64_t per_tiles = (tiles + S - 1) / S;
   *kps = (int)(per_tiles * kTileKeys);
   return (int)((keys + *kps - 1) / *kps);

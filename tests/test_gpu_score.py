@@ -378,3 +378,42 @@ def test_layers_fp32_operands(rows):
     torch.cuda.synchronize()
     ref = oracle.score_rows_for_config([(p.q_text, p.k) for p in ps], ps[0].q_pos0, cfg.n_vis, cfg.hkv, rows)
     _compare(out.cpu().numpy().reshape(-1, cfg.n_vis), ref, f"tiny fp32 x3 {rows}", rel_tol=F32_REL_TOL)
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 5, 7, 8, 12]))
+    T = int(rng.integers(1, 129))
+    wide = seed % 3 == 0  # visual ranges past 16384 keys take eight pass-2 waves
+    n_vis = int(rng.integers(16384, 17500)) if wide else int(rng.integers(1, 3000))
+    pre, post = int(rng.integers(0, 40)), int(rng.integers(0, 40))
+    layers = int(rng.integers(1, 3 if wide else 5))
+    agg = str(rng.choice(["qhead", "kvhead", "all"]))
+    mean = bool(rng.integers(0, 2)) and agg != "qhead"
+    return D, Hkv, G, T, n_vis, pre, post, layers, agg, mean
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_layers_random_shapes(seed):
+    """Seeded random shapes through svlm_score_layers against the oracle:
+    head dims, group sizes that are not powers of two (idle waves), ragged
+    text rows, keys before and after the visual window, one to four layers,
+    every aggregation, with and without the layer mean, and visual ranges on
+    both sides of the eight-wave threshold."""
+    from visual_kv_pruning_amd import ops
+    D, Hkv, G, T, n_vis, pre, post, layers, agg, mean = _random_case(seed)
+    Hq = G * Hkv
+    q_pos0 = pre + n_vis + post
+    n_ctx = q_pos0 + T
+    rng = np.random.default_rng(seed)
+    q = W.bf16_round(rng.standard_normal((layers, T, Hq, D)).astype(np.float32))
+    k = W.bf16_round(rng.standard_normal((layers, Hkv, n_ctx, D)).astype(np.float32))
+    log(f"score_layers case random {seed}: D{D} Hkv{Hkv} G{G} T{T} n_vis{n_vis} pre{pre} post{post} "
+        f"layers{layers} {agg} mean={mean}")
+    out = ops.score_layers(dev_bf16(q), dev_bf16(k), q_pos0, n_vis, vis_start=pre, agg=agg, layer_mean=mean)
+    torch.cuda.synchronize()
+    refs = [_ref(_Layer(q[l], k[l], q_pos0), _Shape(n_vis, Hkv), agg, n_vis, pre) for l in range(layers)]
+    ref = np.mean(refs, axis=0) if mean else np.concatenate(refs, axis=0)
+    _compare(out.cpu().numpy().reshape(ref.shape), ref, f"random {seed}")

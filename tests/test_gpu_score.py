@@ -177,6 +177,31 @@ def test_edge_shapes(D, T, n_vis, pre, post, Hq, Hkv):
                  f"edge {agg}")
 
 
+@pytest.mark.parametrize("T,n_vis,Hq,Hkv", [
+    (96, 16500, 5, 1),   # 5 heads x 6 row blocks over 8 waves: 4 or 3 units each, both passes
+    (64, 3000, 7, 1),    # 7 x 4 units; pass 2 on 4 waves in two workgroups (4 and 3 units per wave)
+    (40, 2000, 6, 2),    # 3 x 3 units over 4 waves: 3, 2, 2, 2
+    (128, 16500, 6, 1),  # 6 x 8 units: pass 1 at 6 per wave; pass 2 keeps a wave per head
+    (20, 2500, 12, 1),   # 12 x 2 units over two workgroups of 8 waves (2 or 1 per wave)
+    (16, 16400, 10, 2),  # 5 units over 8 waves: waves 5-7 hold none
+])
+def test_unit_form_shapes(T, n_vis, Hq, Hkv):
+    """Group sizes that are not a multiple of the waves run the passes over
+    (q head, row block) units spread round-robin over the waves; every
+    aggregation against the oracle (per-head rows keep a wave per head in
+    pass 2, after a unit-form pass 1)."""
+    D, pre, post = 128, 7, 5
+    rng = np.random.default_rng(T * 100 + Hq)
+    q_pos0 = pre + n_vis + post
+    q = W.bf16_round(rng.standard_normal((T, Hq, D)).astype(np.float32))
+    k = W.bf16_round(rng.standard_normal((Hkv, q_pos0 + T, D)).astype(np.float32))
+    p, shape = _Layer(q, k, q_pos0), _Shape(n_vis, Hkv)
+    log(f"score case units T{T} n_vis{n_vis} Hq{Hq} Hkv{Hkv}")
+    for agg in ("qhead", "kvhead", "all"):
+        _compare(_gpu_score(p, shape, agg, n_vis=n_vis, vis_start=pre), _ref(p, shape, agg, n_vis, pre),
+                 f"units {agg}")
+
+
 def test_hour_long_layer_sampled_kv_heads():
     """The hour-long shape (141120 visual + 64 text tokens, 28 q / 4 KV heads)
     at full size with one row per KV head, the signal its per-(layer, KV head)

@@ -12,16 +12,18 @@
 //           P = exp2(c*s - lse2) and sum it over the text rows;
 //   agg:    mean over heads as requested, out = alpha*agg + beta*out.
 //
-// A workgroup owns one KV head and one key range, with one wave per q head of
-// the KV group (up to 8).  The key tile (64 keys) is staged HBM -> LDS once by
+// A workgroup owns one KV head and one key range.  Its waves (up to 8) share
+// the group's (q head, 16-row text block) units: round-robin over the waves
+// where a wave per head would leave waves idle, else one head per wave.  The
+// key tile (64 keys) is staged HBM -> LDS once by
 // LDS-DMA transfers that all waves share (one barrier per tile), so K is read
-// from memory once per workgroup; the text queries of a wave's head sit in
+// from memory once per workgroup; the text queries of a wave's units sit in
 // registers.  Both passes use v_mfma_f32_16x16x32_bf16 with fp32 accumulation
 // and compute S^T (lane = one text row x 4 keys per 16-key block, so a lane
 // needs one log-sum-exp per row block).  Pass 1 keeps a lazily raised
 // reference maximum per lane group, so a key costs one fma, one exp2 and one
 // add; pass 2 adds a lane's row blocks in registers and the 16 row lanes of
-// each key through LDS, and the waves add their heads through LDS.  Several
+// each key through LDS, and the waves add their units through LDS.  Several
 // layers can share one launch of each pass.
 #include <cmath>
 
@@ -34,6 +36,7 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kTileKeys = 64;      // keys per staged K tile
 constexpr float kRescaleSum = 256.f;  // a lane's 4-key weight sum above this raises its reference maximum
 constexpr int kLseBatch = 32;      // pass-1 partials per row loaded at once when a row's log-sum-exp is formed
+constexpr int kUnits2Max8 = 4;     // pass 2 with eight waves: most units per wave in the unit form
 
 struct ScoreArgs {
   const uint16_t* q;
@@ -125,13 +128,20 @@ constexpr int score_ring_depth() {
 // Staging of the K tiles of one (KV head, key range) through a ring of NS
 // slots in LDS: every wave issues its share (PW transfers of 1 KB) of each
 // tile; rows are XOR-swizzled by 16-byte chunk (chunk p of row r holds source
-// chunk p ^ (r % CH)).  Tiles past the range deliver zeros.
+// chunk p ^ (r % CH)).  Tiles past the range deliver zeros.  Transfer i of
+// wave w moves the tile's 1 KB piece i W + w.  When W is a multiple of 4 (or
+// at D = 64, where a piece spans whole swizzle periods) every piece a lane
+// moves has the same row phase, so one per-lane source offset serves all of
+// them and the piece's first row enters as the scalar offset (no per-transfer
+// offset registers to keep live through the key loop).
 template <int D, int W, int NS>
 struct KRing {
   static constexpr int ROWB = D * 2, CH = ROWB / 16;
   static constexpr int TB = kTileKeys * ROWB;
   static constexpr int NI = TB / 1024;
   static constexpr int PW = NI / W;
+  static constexpr int RPT = 1024 / ROWB;  // rows per transfer
+  static constexpr bool kOneOffset = (CH <= RPT) || (W % (CH / RPT) == 0);
   static_assert(PW >= 1 && NI % W == 0, "tile transfers must split evenly over the waves");
   static_assert((NS - 1) * PW <= 63, "ring depth");
   static constexpr int kMaxPW = 16;  // one wave staging a whole D = 128 tile
@@ -139,9 +149,9 @@ struct KRing {
   __amdgpu_buffer_rsrc_t rs;
   unsigned char* lds;
   int wave, row_bytes;
-  // per-lane source offset of each of this wave's PW transfers (set by init;
-  // a fixed bound: sized by PW, the host pass of this compiler dropped the
-  // kernels' launch stubs)
+  // per-lane source offset of each of this wave's PW transfers (only the
+  // first when kOneOffset; a fixed bound: sized by the template parameters,
+  // the host pass of this compiler dropped the kernels' launch stubs)
   int src_lane[kMaxPW];
 
   __device__ void init(const uint16_t* k_rows, int n_rows, int64_t k_sn, unsigned char* ring, int w) {
@@ -151,28 +161,26 @@ struct KRing {
     lds = ring;
     wave = w;
 #pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int r = (wave * PW + i) * (1024 / ROWB) + lane / CH;
+    for (int i = 0; i < (kOneOffset ? 1 : PW); ++i) {
+      const int r = (i * W + wave) * RPT + lane / CH;
       const int p = lane % CH;
-      src_lane[i] = r * row_bytes + ((p ^ (r % CH)) * 16);
+      src_lane[i] = (kOneOffset ? lane / CH : r) * row_bytes + ((p ^ (r % CH)) * 16);
     }
   }
-  __device__ void stage_to(unsigned char* dst, int tile) const {
+  __device__ __forceinline__ void stage_to(unsigned char* dst, int tile) const {
     const int soff = tile * kTileKeys * row_bytes;
 #pragma unroll
-    for (int i = 0; i < PW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(dst + (wave * PW + i) * 1024), 16, src_lane[i],
-          soff, 0, kNT);
+    for (int i = 0; i < PW; ++i) {
+      const int piece = i * W + wave;
+      if constexpr (kOneOffset)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + piece * 1024), 16,
+                                                 src_lane[0], soff + piece * RPT * row_bytes, 0, kNT);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + piece * 1024), 16,
+                                                 src_lane[i], soff, 0, kNT);
+    }
   }
-  __device__ void stage(int slot, int tile) const {
-    const int soff = tile * kTileKeys * row_bytes;
-#pragma unroll
-    for (int i = 0; i < PW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds + slot * TB + (wave * PW + i) * 1024), 16, src_lane[i],
-          soff, 0, kNT);
-  }
+  __device__ __forceinline__ void stage(int slot, int tile) const { stage_to(lds + slot * TB, tile); }
   // LDS byte offset (within a slot) of the lane's K operand chunk: key row r, d chunk kk*4 + g4
   static __device__ unsigned koff(int r, int kk, int g4) { return r * ROWB + (((kk * 4 + g4) ^ (r % CH)) * 16); }
 };
@@ -199,26 +207,80 @@ __device__ __forceinline__ void read_k_pair(unsigned base, const unsigned (&ko)[
   }
 }
 
-// this wave's head's text queries: lane (c, g4) holds row 16 rb + c, d = 32 kk + 8 g4 .. + 7
-// (rows past T read zeros)
-template <int D, int RB>
-__device__ __forceinline__ void load_q(const ScoreArgs& a, int h, u32x4 (&q)[RB][D / 32]) {
+// Work units of a KV group: (q head, 16-row block of the text).
+//  - Unit form: unit u (head u / RBT, row block u % RBT, RBT = row blocks of
+//    T) goes to wave slot u mod (HG W) of the group's HG workgroups of W
+//    waves, so every wave holds U or U - 1 units, U = ceil(G RBT / (HG W)).
+//    With a wave per head, five heads per KV head left three of eight waves
+//    idle and two SIMDs carrying two heads each; seven left one SIMD at half
+//    the load of the others.
+//  - Head form (pass 2 with one output row per q head): wave hl = hg W + w
+//    holds the U row blocks of head hl (none past the group).
+// A unit's text queries sit in registers as the B operand of S^T = K Q^T.
+template <bool UNITS>
+struct WaveUnits {
+  int n;                       // units of this wave (wave-uniform)
+  int slot, stride, total, rbt, g0, G;
+  __device__ WaveUnits(const ScoreArgs& a, int g, int hg, int HG, int W, int wave, int U) {
+    G = a.G;
+    g0 = g * a.G;
+    slot = hg * W + wave;
+    rbt = (a.T + 15) / 16;
+    if constexpr (UNITS) {
+      stride = HG * W;
+      total = a.G * rbt;
+      n = (total > slot) ? (total - slot + stride - 1) / stride : 0;
+    } else {
+      stride = 0;
+      total = 0;
+      n = (slot < a.G) ? U : 0;
+    }
+  }
+  // q head (global index) and first text row of unit i of this wave; units
+  // past n repeat the wave's last one (their results are never used)
+  __device__ __forceinline__ void at(int i, int& head, int& row0) const {
+    if constexpr (UNITS) {
+      const int u = min(slot + stride * i, total - 1);
+      const int hl = u / rbt;
+      head = g0 + hl;
+      row0 = (u - hl * rbt) * 16;
+    } else {
+      head = g0 + min(slot, G - 1);
+      row0 = 16 * i;
+    }
+  }
+};
+
+// one unit's text queries: lane (c, g4) holds row row0 + c, d = 32 kk + 8 g4 .. + 7 (rows past T read zeros)
+template <int D>
+__device__ __forceinline__ void load_q_unit(const ScoreArgs& a, int h, int row0, u32x4 (&q)[D / 32]) {
   const int lane = threadIdx.x & 63, c = lane & 15, g4 = lane >> 4;
   const int bytes = (int)(((int64_t)(a.T - 1) * a.q_st + D) * 2);
   const __amdgpu_buffer_rsrc_t qrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + (int64_t)h * a.q_sh), (short)0, bytes, kBufferFlags);
+  const int t = row0 + c;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int t = rb * 16 + c;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int off = (t < a.T) ? (int)(((int64_t)t * a.q_st + 32 * kk + 8 * g4) * 2) : bytes;
-      q[rb][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-    }
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const int off = (t < a.T) ? (int)(((int64_t)t * a.q_st + 32 * kk + 8 * g4) * 2) : bytes;
+    q[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   }
 }
 
-template <int D, int RB, int W, int NS>
+// Runs f(integral_constant<C>) with C the wave's unit count: U, U - 1 (unit
+// form) or 0, so the key loops are unrolled over exactly the units a wave holds.
+template <int U, bool UNITS, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if (n == U) {
+    f(std::integral_constant<int, U>{});
+  } else if constexpr (UNITS && U > 1) {
+    if (n == U - 1) f(std::integral_constant<int, U - 1>{});
+    else f(std::integral_constant<int, 0>{});
+  } else {
+    f(std::integral_constant<int, 0>{});
+  }
+}
+
+template <int D, int U, int W, int NS, bool UNITS>
 __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   constexpr int KK = D / 32;
   using Ring = KRing<D, W, NS>;
@@ -228,11 +290,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   int layer, g, hg, s;
   if (!decode_block((int)blockIdx.x, a0.S1, a0.Hkv, a0.HG1, a0.layers, layer, g, hg, s)) return;
   const ScoreArgs a = layer_args(a0, layer);
-  const int hl = hg * W + wave;  // head within the KV group
-  // waves past the group (W rounds G up to a power of two) stage their share
-  // of every K tile and meet every barrier, but skip the arithmetic
-  const bool active = hl < a.G;
-  const int h = g * a.G + min(hl, a.G - 1);
+  const WaveUnits<UNITS> wu(a, g, hg, a.HG1, W, wave, U);
 
   const int k_begin = s * a.kps1;
   const int k_end = min(k_begin + a.kps1, a.q_pos0 + a.T);
@@ -241,13 +299,6 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   __shared__ __align__(16) unsigned char ring[NS * Ring::TB];
   Ring kr;
   kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)k_begin * a.k_sn, max(k_end - k_begin, 0), a.k_sn, ring, wave);
-
-  u32x4 qreg[RB][KK];
-  load_q<D, RB>(a, h, qreg);
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
-  wait_vmcnt<(NS - 1) * Ring::PW>();  // the query loads, issued first, have landed
-
   // tiles below n_full are visible to every row and lie inside the range
   const int vis_all = min(k_end, a.q_pos0 + 1) - k_begin;
   const int n_full = min(n_tiles, vis_all > 0 ? vis_all / kTileKeys : 0);
@@ -257,98 +308,118 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass1(ScoreArgs a0) {
   for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
   const unsigned ring0 = lds_addr(ring);
 
-  // per lane group: reference maximum in log2 units of the scaled score, sum
-  float mc[RB], l[RB];
+  // every wave stages its share of every K tile and meets every barrier; a
+  // wave with no units skips the arithmetic
+  with_count<U, UNITS>(wu.n, [&](auto cnt) __attribute__((always_inline)) {
+    constexpr int C = decltype(cnt)::value;
+    constexpr int CQ = C > 0 ? C : 1;
+    int uh[CQ], ur[CQ];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    mc[rb] = kNegInf;
-    l[rb] = 0.f;
-  }
+    for (int i = 0; i < CQ; ++i) wu.at(i, uh[i], ur[i]);
+    u32x4 qreg[CQ][KK];
+    if constexpr (C > 0) {
+#pragma unroll
+      for (int i = 0; i < C; ++i) load_q_unit<D>(a, uh[i], ur[i], qreg[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) kr.stage(u, u);
+    wait_vmcnt<(NS - 1) * Ring::PW>();  // the query loads, issued first, have landed
 
-  auto tile = [&](int t, bool masked) {
-    wait_vmcnt<(NS - 2) * Ring::PW>();  // this wave's share of tile t has landed
-    wg_barrier();                       // every share of tile t has landed; tile t-1 is retired
-    kr.stage((t + NS - 1) % NS, t + NS - 1);
-    if (!active) return;
-    const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
-    u32x4 kq2[2][KK];  // K operands of two blocks per LDS wait
+    // per unit and lane group: reference maximum in log2 units of the scaled score, sum
+    float mc[CQ], l[CQ];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {  // one 16-key block of products at a time keeps the live registers low
-      if (kb % 2 == 0) read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq2);
-      const u32x4 (&kq)[KK] = kq2[kb % 2];
-      const int key0 = k_begin + t * kTileKeys + 16 * kb;
+    for (int i = 0; i < CQ; ++i) {
+      mc[i] = kNegInf;
+      l[i] = 0.f;
+    }
+
+    auto tile = [&](int t, bool masked) __attribute__((always_inline)) {
+      wait_vmcnt<(NS - 2) * Ring::PW>();  // this wave's share of tile t has landed
+      wg_barrier();                       // every share of tile t has landed; tile t-1 is retired
+      kr.stage((t + NS - 1) % NS, t + NS - 1);
+      if constexpr (C > 0) {
+        const unsigned base = ring0 + (unsigned)((t % NS) * Ring::TB);
+        u32x4 kq2[2][KK];  // K operands of two blocks per LDS wait
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) {  // one 16-key block of products at a time keeps the live registers low
+          if (kb % 2 == 0) read_k_pair<KK, 16 * Ring::ROWB>(base + (unsigned)(kb * 16 * Ring::ROWB), ko, kq2);
+          const u32x4 (&kq)[KK] = kq2[kb % 2];
+          const int key0 = k_begin + t * kTileKeys + 16 * kb;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s0 = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), s0);
-        float x[4];
-        if (masked) {
-          const int tq = rb * 16 + c;
-          const int lim = min(k_end, (tq < a.T) ? a.q_pos0 + tq + 1 : 0);  // keys < lim visible to the row
+          for (int i = 0; i < C; ++i) {
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (key0 + 4 * g4 + e < lim) ? s0[e] : kNegInf;
-        } else {
+            for (int kk = 0; kk < KK; ++kk) s0 = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[i][kk]), s0);
+            float x[4];
+            if (masked) {
+              const int tq = ur[i] + c;
+              const int lim = min(k_end, (tq < a.T) ? a.q_pos0 + tq + 1 : 0);  // keys < lim visible to the row
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = s0[e];
+              for (int e = 0; e < 4; ++e) x[e] = (key0 + 4 * g4 + e < lim) ? s0[e] : kNegInf;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = s0[e];
+            }
+            // weights against the current reference: the 4-key sum exceeds
+            // kRescaleSum = 2^8 (or is inf / NaN: no reference yet) only when a
+            // score passes the reference by about 8 (log2 units); the reference is
+            // then raised to the block maximum and the weights recomputed.  The
+            // maximum is taken only on that rare path, so the hot path is one
+            // fma, one exp2 and one add per score.
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, -mc[i]));
+            float s4 = (p[0] + p[1]) + (p[2] + p[3]);
+            if (!(s4 <= kRescaleSum)) {
+              const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * a.c;
+              const float m_new = fmaxf(mc[i], lmax);
+              l[i] *= (mc[i] == kNegInf) ? 0.f : fast_exp2(mc[i] - m_new);
+              mc[i] = m_new;
+              const float mneg = (m_new == kNegInf) ? 0.f : -m_new;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
+              s4 = (p[0] + p[1]) + (p[2] + p[3]);
+            }
+            l[i] += s4;
+          }
         }
-        // weights against the current reference: the 4-key sum exceeds
-        // kRescaleSum = 2^8 (or is inf / NaN: no reference yet) only when a
-        // score passes the reference by about 8 (log2 units); the reference is
-        // then raised to the block maximum and the weights recomputed.  The
-        // maximum is taken only on that rare path, so the hot path is one
-        // fma, one exp2 and one add per score.
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, -mc[rb]));
-        float s4 = (p[0] + p[1]) + (p[2] + p[3]);
-        if (!(s4 <= kRescaleSum)) {
-          const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * a.c;
-          const float m_new = fmaxf(mc[rb], lmax);
-          l[rb] *= (mc[rb] == kNegInf) ? 0.f : fast_exp2(mc[rb] - m_new);
-          mc[rb] = m_new;
-          const float mneg = (m_new == kNegInf) ? 0.f : -m_new;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(x[e], a.c, mneg));
-          s4 = (p[0] + p[1]) + (p[2] + p[3]);
-        }
-        l[rb] += s4;
       }
-    }
-  };
-  int t = 0;
-  for (; t < n_full; ++t) tile(t, false);
-  for (; t < n_tiles; ++t) tile(t, true);
-  wait_vmcnt<0>();
+    };
+    int t = 0;
+    for (; t < n_full; ++t) tile(t, false);
+    for (; t < n_tiles; ++t) tile(t, true);
+    wait_vmcnt<0>();
 
-  // merge the four lane groups (fixed order) and write this split's row state
-  // (maximum back in raw-score units)
+    // merge the four lane groups (fixed order) and write this split's row
+    // state (maximum back in raw-score units)
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float m = (mc[rb] == kNegInf) ? kNegInf : mc[rb] / a.c, ll = l[rb];
-    {
-      const auto mr = __builtin_amdgcn_permlane16_swap(f_bits(m), f_bits(m), false, false);
-      const auto lr = __builtin_amdgcn_permlane16_swap(f_bits(ll), f_bits(ll), false, false);
-      float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
-      merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
-      m = m0;
-      ll = l0;
+    for (int i = 0; i < C; ++i) {
+      float m = (mc[i] == kNegInf) ? kNegInf : mc[i] / a.c, ll = l[i];
+      {
+        const auto mr = __builtin_amdgcn_permlane16_swap(f_bits(m), f_bits(m), false, false);
+        const auto lr = __builtin_amdgcn_permlane16_swap(f_bits(ll), f_bits(ll), false, false);
+        float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
+        merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
+        m = m0;
+        ll = l0;
+      }
+      {
+        const auto mr = __builtin_amdgcn_permlane32_swap(f_bits(m), f_bits(m), false, false);
+        const auto lr = __builtin_amdgcn_permlane32_swap(f_bits(ll), f_bits(ll), false, false);
+        float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
+        merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
+        m = m0;
+        ll = l0;
+      }
+      const int tq = ur[i] + c;
+      if (g4 == 0 && tq < a.T) *(float2*)(a.ml + (((int64_t)uh[i] * a.S1 + s) * a.T + tq) * 2) = make_float2(m, ll);
     }
-    {
-      const auto mr = __builtin_amdgcn_permlane32_swap(f_bits(m), f_bits(m), false, false);
-      const auto lr = __builtin_amdgcn_permlane32_swap(f_bits(ll), f_bits(ll), false, false);
-      float m0 = bits_f(mr[0]), l0 = bits_f(lr[0]);
-      merge_ml(m0, l0, bits_f(mr[1]), bits_f(lr[1]), a.c);
-      m = m0;
-      ll = l0;
-    }
-    const int tq = rb * 16 + c;
-    if (g4 == 0 && active && tq < a.T)
-      *(float2*)(a.ml + (((int64_t)h * a.S1 + s) * a.T + tq) * 2) = make_float2(m, ll);
-  }
+  });
 }
 
-template <int D, int RB, int W, int NS>
+// Pass 2.  Units (group sums): a wave adds the column weights of all its
+// units, whatever their heads; per-head output rows take the head form.
+template <int D, int U, int W, int NS, bool UNITS>
 __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   constexpr int KK = D / 32;
   using Ring = KRing<D, W, NS>;
@@ -358,9 +429,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   int layer, g, hg, s;
   if (!decode_block((int)blockIdx.x, a0.S2, a0.Hkv, a0.HG2, a0.layers, layer, g, hg, s)) return;
   const ScoreArgs a = layer_args(a0, layer);
-  const int hl = hg * W + wave;
-  const bool active = hl < a.G;
-  const int h = g * a.G + min(hl, a.G - 1);
+  const WaveUnits<UNITS> wu(a, g, hg, a.HG2, W, wave, U);
 
   const int v_begin = a.vis_start + s * a.kps2;
   const int v_end = min(v_begin + a.kps2, a.vis_start + a.n_vis);
@@ -370,30 +439,43 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   __shared__ __align__(16) unsigned char ring[Ring::TB];
   __shared__ __align__(16) unsigned char ring_b[Ring::TB];
   __shared__ __align__(16) unsigned char ring_c[Ring::TB];
-  __shared__ float sm_lse[W][RB * 16];
+  __shared__ float sm_lse[W][U * 16];
   __shared__ float xch[2][W][kTileKeys];
   __shared__ __align__(16) float red[W][kTileKeys][20];
   Ring kr;
   kr.init(a.k + (int64_t)g * a.k_sh + (int64_t)v_begin * a.k_sn, max(v_end - v_begin, 0), a.k_sn, ring, wave);
 
-  // Row log-sum-exp (log2 units of the scaled score) from the pass-1
-  // partials, in split order; padded rows get +inf and so contribute
-  // exp2(-inf) = 0.  Lane = row, so each load reads consecutive rows of one
-  // split (the partials are split-major).  The first kLseBatch partials of
-  // the lane's rows are loaded before anything else, so their round trip
-  // waits behind no other load (memory operations complete in issue order);
-  // the K tiles are staged behind them, and the queries are loaded once the
-  // partials are merged, when their registers are free.
-  constexpr int RPL = (RB * 16 + 63) / 64;  // rows per lane
+  // Row log-sum-exp (log2 units of the scaled score) of the wave's unit rows
+  // from the pass-1 partials, in split order; padded rows and units past the
+  // wave's count get +inf and so contribute exp2(-inf) = 0.  Lane = one row
+  // of one unit (the 16 rows of a unit are consecutive rows of one head, so
+  // each load reads consecutive rows of one split: the partials are
+  // split-major).  The first kLseBatch partials of the lane's rows are loaded
+  // before anything else, so their round trip waits behind no other load
+  // (memory operations complete in issue order); the K tiles are staged
+  // behind them, and the queries are loaded once the partials are merged,
+  // when their registers are free.
+  constexpr int RPL = (U * 16 + 63) / 64;  // rows per lane
   float M[RPL], L[RPL];
+  int row_ok[RPL];
+  int64_t row_off[RPL];  // float offset of the lane's row in split 0 of the partials
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int rho = lane + 64 * r;
+    const int i = min(rho >> 4, U - 1);
+    int h, r0;
+    wu.at(i, h, r0);
+    const int tq = r0 + (rho & 15);
+    row_ok[r] = (rho < U * 16) && (i < wu.n) && (tq < a.T);
+    row_off[r] = ((int64_t)h * a.S1 * a.T + min(tq, a.T - 1)) * 2;
+  }
   auto load_parts = [&](int s0, float2 (&part)[RPL][kLseBatch]) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int tq = lane + 64 * r;
-      const float2* p = (const float2*)(a.ml + ((int64_t)h * a.S1 * a.T + min(tq, a.T - 1)) * 2);
+      const float2* p = (const float2*)(a.ml + row_off[r]);
 #pragma unroll
       for (int j = 0; j < kLseBatch; ++j)
-        part[r][j] = (tq < a.T && s0 + j < a.S1) ? p[(int64_t)(s0 + j) * a.T] : make_float2(kNegInf, 0.f);
+        part[r][j] = (row_ok[r] && s0 + j < a.S1) ? p[(int64_t)(s0 + j) * a.T] : make_float2(kNegInf, 0.f);
     }
   };
   // a batch of partials joins the running (M, L) in two steps: the largest
@@ -433,20 +515,10 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
   }
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int tq = lane + 64 * r;
-    if (tq < RB * 16) sm_lse[wave][tq] = (tq < a.T && L[r] > 0.f) ? M[r] * a.c + log2f(L[r]) : INFINITY;
+    const int rho = lane + 64 * r;
+    if (rho < U * 16) sm_lse[wave][rho] = (row_ok[r] && L[r] > 0.f) ? M[r] * a.c + log2f(L[r]) : INFINITY;
   }
 
-  u32x4 qreg[RB][KK];
-  load_q<D, RB>(a, h, qreg);
-  wait_lgkmcnt0();
-  float lse_t[RB];  // the lane's text rows 16 rb + c
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) lse_t[rb] = sm_lse[wave][rb * 16 + c];
-
-  unsigned ko[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
   const float invT = 1.f / (float)a.T;
   const bool direct = !a.layer_mean && ((a.agg == SVLM_AGG_QHEAD) || (a.agg == SVLM_AGG_KVHEAD && a.HG2 == 1));
   // the KV-head mean is taken here when one workgroup holds the whole group, else by score_agg
@@ -463,7 +535,7 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
       a.grp[(int64_t)row * a.n_vis + i] = v;
     }
   };
-  // wave 0 adds the waves' column means of tile tt (published in xch[tt % 2])
+  // wave 0 adds the waves' column sums of tile tt (published in xch[tt % 2])
   auto flush = [&](int tt) {
     if (wave != 0) return;
     const int key = v_begin + tt * kTileKeys + lane;
@@ -472,65 +544,91 @@ __global__ __launch_bounds__(64 * W, 1) void score_pass2(ScoreArgs a0) {
     for (int w = 0; w < W; ++w) v += xch[tt & 1][w][lane];
     if (key < v_end) emit(direct ? g : g * a.HG2 + hg, key, v * grp_scale);
   };
+  const bool qhead = !UNITS && a.agg == SVLM_AGG_QHEAD;
 
-  auto body = [&](int t, const unsigned char* rd, unsigned char* dma) __attribute__((always_inline)) {
-    wait_vmcnt<(NS - 2) * Ring::PW>();
-    wait_lgkmcnt0();  // this wave's column means of tile t-1 are in LDS
-    wg_barrier();
-    kr.stage_to(dma, t + NS - 1);
-    if (a.agg != SVLM_AGG_QHEAD && t > 0) flush(t - 1);
-    const int key = v_begin + t * kTileKeys + lane;
-    if (!active) {  // waves past the group add nothing
-      if (a.agg != SVLM_AGG_QHEAD) xch[t & 1][wave][lane] = 0.f;
-      return;
-    }
+  with_count<U, UNITS>(wu.n, [&](auto cnt) __attribute__((always_inline)) {
+    constexpr int C = decltype(cnt)::value;
+    constexpr int CQ = C > 0 ? C : 1;
+    u32x4 qreg[CQ][KK];
+    float lse_t[CQ];  // the lane's text row of each unit
+    int h_out = 0;
+    if constexpr (C > 0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4 kq[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kq[kk] = *(const u32x4*)(rd + kb * 16 * Ring::ROWB + ko[kk]);
-      f32x4 S[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) S[rb] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[rb][kk]), S[rb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float e[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) e[rb] = fast_exp2(fmaf(S[rb][i], a.c, -lse_t[rb]));
-#pragma unroll
-        for (int w2 = 1; w2 < RB; w2 *= 2)
-#pragma unroll
-          for (int rb = 0; rb + w2 < RB; rb += 2 * w2) e[rb] += e[rb + w2];
-        red[wave][16 * kb + 4 * g4 + i][c] = e[0];
+      for (int i = 0; i < C; ++i) {
+        int h, r0;
+        wu.at(i, h, r0);
+        load_q_unit<D>(a, h, r0, qreg[i]);
+        h_out = h;
       }
     }
-    float4 rr[4];
+    wait_lgkmcnt0();
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) rr[q4] = *(const float4*)&red[wave][lane][4 * q4];
-    float v = 0.f;
+    for (int i = 0; i < CQ; ++i) lse_t[i] = sm_lse[wave][i * 16 + c];
+
+    unsigned ko[KK];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) v = (((v + rr[q4].x) + rr[q4].y) + rr[q4].z) + rr[q4].w;
-    v *= invT;
-    if (a.agg == SVLM_AGG_QHEAD) {
-      if (active && key < v_end) emit(h, key, v);
-    } else {
-      xch[t & 1][wave][lane] = active ? v : 0.f;
+    for (int kk = 0; kk < KK; ++kk) ko[kk] = Ring::koff(c, kk, g4);
+
+    auto body = [&](int t, const unsigned char* rd, unsigned char* dma) __attribute__((always_inline)) {
+      wait_vmcnt<(NS - 2) * Ring::PW>();
+      wait_lgkmcnt0();  // this wave's column sums of tile t-1 are in LDS
+      wg_barrier();
+      kr.stage_to(dma, t + NS - 1);
+      if (!qhead && t > 0) flush(t - 1);
+      const int key = v_begin + t * kTileKeys + lane;
+      if constexpr (C == 0) {  // a wave with no units adds nothing
+        if (!qhead) xch[t & 1][wave][lane] = 0.f;
+        return;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          u32x4 kq[KK];
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) kq[kk] = *(const u32x4*)(rd + kb * 16 * Ring::ROWB + ko[kk]);
+          f32x4 S[C];
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) S[i] = mfma16(as_bf16x8(kq[kk]), as_bf16x8(qreg[i][kk]), S[i]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float e[C];
+#pragma unroll
+            for (int i = 0; i < C; ++i) e[i] = fast_exp2(fmaf(S[i][q], a.c, -lse_t[i]));
+#pragma unroll
+            for (int w2 = 1; w2 < C; w2 *= 2)
+#pragma unroll
+              for (int i = 0; i + w2 < C; i += 2 * w2) e[i] += e[i + w2];
+            red[wave][16 * kb + 4 * g4 + q][c] = e[0];
+          }
+        }
+        float4 rr[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) rr[q4] = *(const float4*)&red[wave][lane][4 * q4];
+        float v = 0.f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) v = (((v + rr[q4].x) + rr[q4].y) + rr[q4].z) + rr[q4].w;
+        v *= invT;
+        if (qhead) {
+          if (key < v_end) emit(h_out, key, v);
+        } else {
+          xch[t & 1][wave][lane] = v;
+        }
+      }
+    };
+    int t = 0;
+    for (; t + 3 <= n_tiles; t += 3) {
+      body(t, ring, ring_c);
+      body(t + 1, ring_b, ring);
+      body(t + 2, ring_c, ring_b);
     }
-  };
-  int t = 0;
-  for (; t + 3 <= n_tiles; t += 3) {
-    body(t, ring, ring_c);
-    body(t + 1, ring_b, ring);
-    body(t + 2, ring_c, ring_b);
-  }
-  if (t < n_tiles) body(t, ring, ring_c);
-  if (t + 1 < n_tiles) body(t + 1, ring_b, ring);
+    if (t < n_tiles) body(t, ring, ring_c);
+    if (t + 1 < n_tiles) body(t + 1, ring_b, ring);
+  });
   wait_vmcnt<0>();
-  if (a.agg != SVLM_AGG_QHEAD && n_tiles > 0) {
+  if (!qhead && n_tiles > 0) {
     wait_lgkmcnt0();
     wg_barrier();
     flush(n_tiles - 1);
@@ -617,39 +715,59 @@ inline int64_t pass_blocks(int layers, int Hkv, int S, int HG) {
   return (mul_sat(mul_sat(layers, Hkv), S) + 7) / 8 * 8 * HG;
 }
 
-template <int D, int RB, int W>
+template <int D, int U, int W, bool UNITS>
 void launch_pass1(const ScoreArgs& a, hipStream_t st) {
-  score_pass1<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING1>()><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
+  score_pass1<D, U, W, score_ring_depth<D, W, SVLM_SCORE_RING1>(), UNITS><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S1, a.HG1), 64 * W, 0, st>>>(a);
 }
-template <int D, int RB, int W>
+template <int D, int U, int W, bool UNITS>
 void launch_pass2(const ScoreArgs& a, hipStream_t st) {
-  score_pass2<D, RB, W, score_ring_depth<D, W, SVLM_SCORE_RING2>()><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
+  score_pass2<D, U, W, score_ring_depth<D, W, SVLM_SCORE_RING2>(), UNITS><<<(unsigned)pass_blocks(a.layers, a.Hkv, a.S2, a.HG2), 64 * W, 0, st>>>(a);
 }
 
-template <int D, int RB>
-void launch_rb(const ScoreArgs& a, int w1, int w2, hipStream_t st) {
-  switch (w1) {
-    case 1: launch_pass1<D, RB, 1>(a, st); break;
-    case 2: launch_pass1<D, RB, 2>(a, st); break;
-    case 4: launch_pass1<D, RB, 4>(a, st); break;
-    default: launch_pass1<D, RB, 8>(a, st); break;
-  }
-  switch (w2) {
-    case 1: launch_pass2<D, RB, 1>(a, st); break;
-    case 2: launch_pass2<D, RB, 2>(a, st); break;
-    case 4: launch_pass2<D, RB, 4>(a, st); break;
-    default: launch_pass2<D, RB, 8>(a, st); break;
+// one pass (PASS 1 or 2) with w waves; U units or row blocks per wave
+template <int D, int PASS, int U, int W, bool UNITS>
+void launch_one(const ScoreArgs& a, hipStream_t st) {
+  if constexpr (PASS == 1) launch_pass1<D, U, W, UNITS>(a, st);
+  else launch_pass2<D, U, W, UNITS>(a, st);
+}
+template <int D, int PASS, int U, bool UNITS>
+void launch_pass(const ScoreArgs& a, int w, hipStream_t st) {
+  if constexpr (UNITS) {  // the unit form runs at D = 128 with 4 or 8 waves (pass 2 with 8: at most 4 units)
+    if constexpr (PASS == 2 && U > kUnits2Max8) launch_one<D, PASS, U, 4, true>(a, st);
+    else if (w == 4) launch_one<D, PASS, U, 4, true>(a, st);
+    else launch_one<D, PASS, U, 8, true>(a, st);
+  } else {
+    switch (w) {
+      case 1: launch_one<D, PASS, U, 1, false>(a, st); break;
+      case 2: launch_one<D, PASS, U, 2, false>(a, st); break;
+      case 4: launch_one<D, PASS, U, 4, false>(a, st); break;
+      default: launch_one<D, PASS, U, 8, false>(a, st); break;
+    }
   }
 }
-
-template <int D>
-void launch_d(const ScoreArgs& a, int rb, int w1, int w2, hipStream_t st) {
+// unit form: u units per wave, 1 .. 8
+template <int PASS>
+void launch_units(const ScoreArgs& a, int u, int w, hipStream_t st) {
+  switch (u) {
+    case 1: launch_pass<128, PASS, 1, true>(a, w, st); break;
+    case 2: launch_pass<128, PASS, 2, true>(a, w, st); break;
+    case 3: launch_pass<128, PASS, 3, true>(a, w, st); break;
+    case 4: launch_pass<128, PASS, 4, true>(a, w, st); break;
+    case 5: launch_pass<128, PASS, 5, true>(a, w, st); break;
+    case 6: launch_pass<128, PASS, 6, true>(a, w, st); break;
+    case 7: launch_pass<128, PASS, 7, true>(a, w, st); break;
+    default: launch_pass<128, PASS, 8, true>(a, w, st); break;
+  }
+}
+// head form: rb row blocks per head (1, 2, 4, 6 or 8)
+template <int D, int PASS>
+void launch_heads(const ScoreArgs& a, int rb, int w, hipStream_t st) {
   switch (rb) {
-    case 1: launch_rb<D, 1>(a, w1, w2, st); break;
-    case 2: launch_rb<D, 2>(a, w1, w2, st); break;
-    case 4: launch_rb<D, 4>(a, w1, w2, st); break;
-    case 6: launch_rb<D, 6>(a, w1, w2, st); break;
-    default: launch_rb<D, 8>(a, w1, w2, st); break;
+    case 1: launch_pass<D, PASS, 1, false>(a, w, st); break;
+    case 2: launch_pass<D, PASS, 2, false>(a, w, st); break;
+    case 4: launch_pass<D, PASS, 4, false>(a, w, st); break;
+    case 6: launch_pass<D, PASS, 6, false>(a, w, st); break;
+    default: launch_pass<D, PASS, 8, false>(a, w, st); break;
   }
 }
 
@@ -674,6 +792,22 @@ int pick_waves(int G, int cap) {
   int w = 1;
   while (w < G && w < cap) w *= 2;
   return w;
+}
+
+// units per wave of the unit form: G heads x ceil(T / 16) row blocks over HG workgroups of W waves
+int units_per_wave(int T, int G, int HG, int W) {
+  const int units = G * ((T + 15) / 16);
+  return (units + HG * W - 1) / (HG * W);
+}
+// The unit form where a wave per head would leave waves idle (the head
+// count of a group is not a multiple of the waves), at D = 128 with 4 or 8
+// waves; the head form elsewhere (and for per-head output rows).  Pass 2 with
+// eight waves takes the unit form up to kUnits2Max8 units per wave: beyond
+// that its registers (two waves per SIMD share the file) spill inside the
+// key loop, where the head form's do not.
+bool use_units(int pass, int D, int T, int G, int HG, int W) {
+  if (D != 128 || W < 4 || HG * W <= G) return false;
+  return pass == 1 || W == 4 || units_per_wave(T, G, HG, W) <= kUnits2Max8;
 }
 
 // key splits: one layer takes about one workgroup per compute unit.  Several
@@ -902,8 +1036,13 @@ static int score_impl(const char* name, const void* q_text, int64_t q_st, int64_
   a.layer_mean = layer_mean;
   a.rows = out_rows;
   const int rb = pick_rb(T);
-  if (D == 128) launch_d<128>(a, rb, gm.W1, gm.W2, st);
-  else launch_d<64>(a, rb, gm.W1, gm.W2, st);
+  if (use_units(1, D, T, a.G, gm.HG1, gm.W1)) launch_units<1>(a, units_per_wave(T, a.G, gm.HG1, gm.W1), gm.W1, st);
+  else if (D == 128) launch_heads<128, 1>(a, rb, gm.W1, st);
+  else launch_heads<64, 1>(a, rb, gm.W1, st);
+  if (agg != SVLM_AGG_QHEAD && use_units(2, D, T, a.G, gm.HG2, gm.W2))
+    launch_units<2>(a, units_per_wave(T, a.G, gm.HG2, gm.W2), gm.W2, st);
+  else if (D == 128) launch_heads<128, 2>(a, rb, gm.W2, st);
+  else launch_heads<64, 2>(a, rb, gm.W2, st);
   if (layer_mean) {
     score_agg_layers<<<dim3((unsigned)((n_vis + 63) / 64), (unsigned)out_rows), 64 * kAggLanes, 0, st>>>(a);
   } else if (!direct) {

@@ -732,7 +732,10 @@ void launch_one(const ScoreArgs& a, hipStream_t st) {
 }
 template <int D, int PASS, int U, bool UNITS>
 void launch_pass(const ScoreArgs& a, int w, hipStream_t st) {
-  if constexpr (UNITS) {  // the unit form runs at D = 128 with 4 or 8 waves (pass 2 with 8: at most 4 units)
+  if constexpr (UNITS) {  // the unit form runs at D = 128 with 4 or 8 waves
+    // pass 2 with eight waves never holds more than kUnits2Max8 units
+    // (use_units sends those shapes to the head form), so w is 4 here and the
+    // eight-wave kernels are not instantiated for them
     if constexpr (PASS == 2 && U > kUnits2Max8) launch_one<D, PASS, U, 4, true>(a, st);
     else if (w == 4) launch_one<D, PASS, U, 4, true>(a, st);
     else launch_one<D, PASS, U, 8, true>(a, st);

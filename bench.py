@@ -138,7 +138,7 @@ def main():
     # the draft's key list for the in-place variant: kept visual rows, then the text and newest rows
     draft_idx = torch.empty(N_draft, dtype=torch.int32, device=dev)
     draft_idx[B_keep:] = torch.arange(NV, NV + T + 1, dtype=torch.int32, device=dev)
-    ws_acc = torch.empty(ops.verify_workspace_bytes(1, gv, V), dtype=torch.uint8, device=dev)
+    ws_acc = torch.zeros(ops.verify_workspace_bytes(1, gv, V), dtype=torch.uint8, device=dev)
     o_v = torch.empty(1, nqv, Hq, D, dtype=torch.float32, device=dev)
     l_v = torch.empty(1, nqv, Hq, dtype=torch.float32, device=dev)
     o_d = torch.empty(1, 1, Hq, D, dtype=torch.float32, device=dev)
@@ -200,9 +200,12 @@ def main():
         "uvprune_score": k_uvprune,
         "verify_attn": lambda: [k_verify_attn(l) for l in range(L)],
         "accept": k_accept,
+        # the same call 16 times in one graph: per-call time without the replay
+        # overhead of a one-node graph (a decode loop runs it between other kernels)
+        "accept_in_sequence": lambda: [k_accept() for _ in range(16)],
     }
     calls = {"score": 1, "score_layer_calls": L, "select": 1, "gather": 1, "draft_attn": L, "draft_attn_indexed": L, "uvprune_score": 1,
-             "verify_attn": L, "accept": 1}
+             "verify_attn": L, "accept": 1, "accept_in_sequence": 16}
 
     # warm up eagerly (also fills the library's device-property cache), then capture
     # each kernel sequence as a HIP graph so host launch overhead is out of the timings
@@ -221,7 +224,8 @@ def main():
     # one step of the path: every kind but the alternatives, timed on their own
     # below (the in-place draft instead of gather + compact draft; the UV-Prune
     # score instead of the attention score)
-    step_kinds = [k for k in seqs if k not in ("draft_attn_indexed", "uvprune_score", "score_layer_calls")]
+    step_kinds = [k for k in seqs if k not in ("draft_attn_indexed", "uvprune_score", "score_layer_calls",
+                                                "accept_in_sequence")]
 
     def step():
         for kind in step_kinds:
@@ -344,7 +348,10 @@ def main():
     acc_bytes = 2 * V * 4
     kernels["accept"].update(bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept"] * 1e-6) / 1e9, 1),
                              what="rejection acceptance, gamma 5, V 152064: bytes = the two probability rows "
-                                  "the draw reads (p_n and q_n); two launches of dependent loads")
+                                  "the draw reads (p_n and q_n); one launch of dependent loads")
+    kernels["accept_in_sequence"].update(
+        bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept_in_sequence"] * 1e-6) / 1e9, 1),
+        what="the same acceptance call, 16 calls in one graph (per call)")
     gather_bytes = L * 2 * 2 * (B_keep + T) * Hkv * D * 2  # every layer's kept K and V rows, read + write
     kernels["gather"].update(bytes=gather_bytes, gbs=round(gather_bytes / (per_us["gather"] * 1e-6) / 1e9, 1),
                              what="one call over all layers (their caches folded into the head axis)")

@@ -357,7 +357,13 @@ int svlm_uvprune_score(const void* v0, const void* vL, int64_t v_sn, int n_vis,
  *   argmax p_i.
  * n_accept, next_tok: [B] int32 outputs.  Requires 1 <= gamma, 1 <= V,
  * draft tokens in [0, V) (clamped otherwise), probabilities in [0, 1].
- * ws: svlm_verify_workspace(batch, gamma, V) bytes.
+ * ws: svlm_verify_workspace(batch, gamma, V) bytes, zero-filled before its
+ *   first use.  Its first 256 KB are arrival counters, one per sequence
+ *   index: the call is one launch whose last workgroup per sequence to finish
+ *   its vocabulary chunk reduces the chunk results (stored after the
+ *   counters), and it leaves the counters zero again, so one workspace, big
+ *   enough for the largest call, serves later calls of any shape without
+ *   clearing.  Calls that share a workspace must not overlap in time.
  * ------------------------------------------------------------------------ */
 size_t svlm_verify_workspace(int batch, int gamma, int V);
 int svlm_verify(int mode, int batch, int gamma, int V, const int32_t* draft_tok,

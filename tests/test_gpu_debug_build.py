@@ -146,7 +146,7 @@ def test_verify_draft_token_outside_the_vocabulary(dbg, mode):
     n_acc = torch.empty(B, dtype=torch.int32, device=DEV)
     nxt = torch.empty(B, dtype=torch.int32, device=DEV)
     wsb = dbg.svlm_verify_workspace(B, gamma, V)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)  # arrival counters start at zero
 
     def run(draft):
         st = dbg.svlm_verify(mode, B, gamma, V, _p(draft), _p(target), _p(q) if q is not None else None,

@@ -108,3 +108,32 @@ def test_long_windows_cross_the_64_position_rounds(first_miss):
     n, t = _gpu("reject", d, p, q, u)
     rn, rt = oracle.verify_reject(d, p, q, u)
     assert np.array_equal(n, rn) and np.array_equal(t, rt)
+
+
+def test_workspace_reused_across_calls_and_modes():
+    """One zero-filled workspace serves a run of calls: each launch's last
+    workgroup per sequence resets its arrival counter, so later calls (either
+    mode, fewer sequences, a longer window) still reduce every chunk."""
+    from visual_kv_pruning_amd import ops
+    V = 152064
+    ws = torch.zeros(ops.verify_workspace_bytes(4, 9, V), dtype=torch.uint8, device="cuda:0")
+    cases = [("reject", 4, 5, 30), ("greedy", 4, 9, 31), ("reject", 1, 9, 32), ("greedy", 2, 3, 33),
+             ("reject", 3, 2, 34), ("reject", 3, 2, 35), ("greedy", 1, 1, 36)]
+    for rep in range(2):
+        for mode, batch, gamma, seed in cases:
+            vi = W.verify_inputs(seed, batch, gamma, V, extra=V)
+            log(f"verify workspace reuse rep={rep} mode={mode} B={batch} gamma={gamma} seed={seed}")
+            if mode == "greedy":
+                d = vi.draft_tok_greedy.copy()
+                d[:, : gamma // 2] = np.argmax(vi.target_logits[:, : gamma // 2], axis=-1)
+                n, t = ops.verify("greedy", _t(d, np.int32), _t(vi.target_logits, np.float32), ws=ws)
+                rn, rt = oracle.verify_greedy(d, vi.target_logits)
+            else:
+                n, t = ops.verify("reject", _t(vi.draft_tok_sampled, np.int32), _t(vi.p, np.float32),
+                                  _t(vi.q, np.float32), _t(vi.u, np.float32), ws=ws)
+                rn, rt = oracle.verify_reject(vi.draft_tok_sampled, vi.p, vi.q, vi.u)
+            torch.cuda.synchronize()
+            assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(t.cpu().numpy(), rt)
+    # every call left the counters zero
+    tail = ws[: 4 * 4].cpu().numpy()
+    assert not tail.any()

@@ -10,9 +10,10 @@
 // bonus from p_gamma.  The draw is a fixed-point (2^-40) inverse CDF, so the
 // result is exact integer arithmetic and independent of reduction order.
 //
-// Two launches per call: a chunk pass spread over the vocabulary (argmax per
-// row for greedy; masses and argmax of the row to draw from for rejection),
-// then one workgroup per sequence that reduces the chunk results in chunk
+// One launch per call: a chunk pass spread over the vocabulary (argmax per
+// row for greedy; masses and argmax of the row to draw from for rejection);
+// the last workgroup of a sequence to finish its chunk (an arrival counter
+// per sequence in the workspace) then reduces the chunk results in chunk
 // order and, for rejection, walks the one chunk where the inverse CDF lands.
 #include <cmath>
 
@@ -69,8 +70,25 @@ struct VerifyArgs {
   ArgMax* g_part;       // greedy: [B][gamma+1][chunks]
   uint64_t* r_mass;     // reject: [B][chunks][2]  (residual-or-bonus row, fallback row)
   ArgMax* r_arg;        // reject: [B][chunks]
-  int32_t* r_first;     // reject: [B] first rejected position (written by chunk 0)
+  uint32_t* arrived;    // [B] arrival counters: zero between calls
 };
+
+// Called by every thread once the workgroup's results are stored (by thread
+// 0).  Counts the workgroup in for sequence b and returns true in all threads
+// of the one workgroup that arrives last, which resets the counter.  The
+// count is an acquire-release atomic at device scope: the results stored
+// before it by every workgroup are visible to the last one after it.
+__device__ __forceinline__ bool arrive_last(const VerifyArgs& a, int b, uint32_t expected) {
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.arrived[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == expected - 1;
+    if (last) __hip_atomic_store(&a.arrived[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last != 0;
+}
 
 __device__ __forceinline__ int clamp_tok(int t, int V) {
   debug_check(t >= 0 && t < V, SVLM_DBG_DRAFT_TOKEN);
@@ -101,36 +119,10 @@ __device__ int first_reject_wave(const VerifyArgs& a, int b) {
   return G;
 }
 
-__global__ __launch_bounds__(kThreads) void greedy_chunks(VerifyArgs a) {
-  const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const float* row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
-  const int base = c * kChunk;
-  // all loads first (indices clamped into the row, so none is conditional), then the reduction
-  float x[kPerThread];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) x[k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
-  ArgMax best = {-INFINITY, 0x7fffffff};
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int v = base + k * kThreads + threadIdx.x;
-    if (v < a.V) best = better(best, ArgMax{x[k], v});
-  }
-  best = wave_argmax(best);
-  __shared__ ArgMax sm[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    ArgMax r = sm[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = better(r, sm[w]);
-    a.g_part[((int64_t)b * (a.gamma + 1) + i) * a.chunks + c] = r;
-  }
-}
-
-// one workgroup per sequence: the waves reduce the chunk results of up to 64
-// rows at a time (a row per wave in turn), then thread 0 walks them in row
-// order to the first draft that differs from the dense argmax
-__global__ __launch_bounds__(kThreads) void greedy_final(VerifyArgs a) {
-  const int b = blockIdx.x;
+// the last workgroup of sequence b: the waves reduce the chunk results of up
+// to 64 rows at a time (a row per wave in turn), then thread 0 walks them in
+// row order to the first draft that differs from the dense argmax
+__device__ void greedy_final(const VerifyArgs& a, int b) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __shared__ int s_am[64];
   __shared__ int s_done;
@@ -168,81 +160,44 @@ __global__ __launch_bounds__(kThreads) void greedy_final(VerifyArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
-  const int c = blockIdx.x, b = blockIdx.y;
-  __shared__ int sm_n;
-  if (threadIdx.x < 64) {
-    const int n0 = first_reject_wave(a, b);
-    if (threadIdx.x == 0) {
-      sm_n = n0;
-      if (c == 0) a.r_first[b] = n0;
-    }
-  }
-  __syncthreads();
-  const int n = sm_n;
-  const int G = a.gamma;
-  const float* prow = a.target + ((int64_t)b * (G + 1) + n) * a.V;
-  const float* qrow = (n < G) ? a.q + ((int64_t)b * G + n) * a.V : nullptr;
+__global__ __launch_bounds__(kThreads) void greedy_chunks(VerifyArgs a) {
+  const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const float* row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
   const int base = c * kChunk;
-  // all loads first (indices clamped into the row, so none is conditional), then the sums
-  float pv[kPerThread], qv[kPerThread];
+  // all loads first (indices clamped into the row, so none is conditional), then the reduction
+  float x[kPerThread];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int v = min(base + k * kThreads + (int)threadIdx.x, a.V - 1);
-    pv[k] = prow[v];
-    qv[k] = qrow ? qrow[v] : 0.f;
-  }
-  uint64_t mw = 0, mp = 0;
+  for (int k = 0; k < kPerThread; ++k) x[k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
   ArgMax best = {-INFINITY, 0x7fffffff};
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int v = base + k * kThreads + threadIdx.x;
-    if (v < a.V) {
-      const float p = pv[k];
-      const float w = qrow ? fmaxf(p - qv[k], 0.f) : p;
-      mw += mass40(w);
-      mp += mass40(p);
-      best = better(best, ArgMax{p, v});
-    }
+    if (v < a.V) best = better(best, ArgMax{x[k], v});
   }
-  mw = wave_sum_u64(mw);
-  mp = wave_sum_u64(mp);
   best = wave_argmax(best);
-  __shared__ uint64_t sw[kThreads / 64], sp[kThreads / 64];
-  __shared__ ArgMax sa[kThreads / 64];
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sw[wv] = mw;
-    sp[wv] = mp;
-    sa[wv] = best;
-  }
+  __shared__ ArgMax sm[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = best;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint64_t tw = 0, tp = 0;
-    ArgMax r = sa[0];
-    for (int w = 0; w < kThreads / 64; ++w) {
-      tw += sw[w];
-      tp += sp[w];
-      if (w) r = better(r, sa[w]);
-    }
-    a.r_mass[((int64_t)b * a.chunks + c) * 2 + 0] = tw;
-    a.r_mass[((int64_t)b * a.chunks + c) * 2 + 1] = tp;
-    a.r_arg[(int64_t)b * a.chunks + c] = r;
+    ArgMax r = sm[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = better(r, sm[w]);
+    a.g_part[((int64_t)b * (a.gamma + 1) + i) * a.chunks + c] = r;
   }
+  if (arrive_last(a, b, (uint32_t)a.chunks * (uint32_t)(a.gamma + 1))) greedy_final(a, b);
 }
 
-__global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
-  const int b = blockIdx.x;
+// the last workgroup of sequence b (first rejection at n, or n == gamma):
+// row totals over the chunk results, the chunk where the inverse CDF with
+// uniform uu lands, then that chunk walked in index order
+__device__ void reject_final(const VerifyArgs& a, int b, int n, double uu) {
   const int G = a.gamma;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  __shared__ int sm_n, sm_mode, sm_chunk, sm_tok;
+  __shared__ int sm_mode, sm_chunk, sm_tok;
   __shared__ uint64_t sm_t;
   __shared__ uint64_t s_excl[kThreads / 64];
   __shared__ uint64_t s_w[kThreads / 64], s_p[kThreads / 64];
   __shared__ ArgMax s_a[kThreads / 64];
-  if (tid == 0) sm_n = a.r_first[b];
-  const double uu = a.u[(int64_t)b * (G + 1) + G];  // in flight with the chunk results
   // row totals over the chunks (chunk-parallel; integer sums are exact in any
   // order); a thread keeps the masses of its first chunk for the ordered scan
   uint64_t mw = 0, mp = 0, first_w = 0, first_p = 0;
@@ -325,7 +280,6 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
     }
   }
   __syncthreads();
-  const int n = sm_n;
   const int mode = sm_mode;
   if (mode == 2) {
     if (tid == 0) {
@@ -378,6 +332,69 @@ __global__ __launch_bounds__(kThreads) void reject_final(VerifyArgs a) {
   }
 }
 
+
+__global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  __shared__ int sm_n;
+  if (threadIdx.x < 64) {
+    const int n0 = first_reject_wave(a, b);
+    if (threadIdx.x == 0) sm_n = n0;
+  }
+  __syncthreads();
+  const int n = sm_n;
+  const int G = a.gamma;
+  const double uu = a.u[(int64_t)b * (G + 1) + G];  // the draw's uniform, used by the last workgroup
+  const float* prow = a.target + ((int64_t)b * (G + 1) + n) * a.V;
+  const float* qrow = (n < G) ? a.q + ((int64_t)b * G + n) * a.V : nullptr;
+  const int base = c * kChunk;
+  // all loads first (indices clamped into the row, so none is conditional), then the sums
+  float pv[kPerThread], qv[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int v = min(base + k * kThreads + (int)threadIdx.x, a.V - 1);
+    pv[k] = prow[v];
+    qv[k] = qrow ? qrow[v] : 0.f;
+  }
+  uint64_t mw = 0, mp = 0;
+  ArgMax best = {-INFINITY, 0x7fffffff};
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int v = base + k * kThreads + threadIdx.x;
+    if (v < a.V) {
+      const float p = pv[k];
+      const float w = qrow ? fmaxf(p - qv[k], 0.f) : p;
+      mw += mass40(w);
+      mp += mass40(p);
+      best = better(best, ArgMax{p, v});
+    }
+  }
+  mw = wave_sum_u64(mw);
+  mp = wave_sum_u64(mp);
+  best = wave_argmax(best);
+  __shared__ uint64_t sw[kThreads / 64], sp[kThreads / 64];
+  __shared__ ArgMax sa[kThreads / 64];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sw[wv] = mw;
+    sp[wv] = mp;
+    sa[wv] = best;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t tw = 0, tp = 0;
+    ArgMax r = sa[0];
+    for (int w = 0; w < kThreads / 64; ++w) {
+      tw += sw[w];
+      tp += sp[w];
+      if (w) r = better(r, sa[w]);
+    }
+    a.r_mass[((int64_t)b * a.chunks + c) * 2 + 0] = tw;
+    a.r_mass[((int64_t)b * a.chunks + c) * 2 + 1] = tp;
+    a.r_arg[(int64_t)b * a.chunks + c] = r;
+  }
+  if (arrive_last(a, b, (uint32_t)a.chunks)) reject_final(a, b, n, uu);
+}
+
 }  // namespace
 }  // namespace svlm
 
@@ -390,12 +407,22 @@ static bool verify_fits(int batch, int gamma, int V) {
   return grid_fits(verify_chunks(V), kThreads, (int64_t)gamma + 1, batch);
 }
 
-extern "C" size_t svlm_verify_workspace(int batch, int gamma, int V) {
-  if (batch < 1 || gamma < 1 || V < 1 || !verify_fits(batch, gamma, V)) return 0;
+// The workspace opens with one arrival counter per possible sequence (the
+// batch stays below 65536), so the counters sit at the same place whatever
+// the call's shape and the chunk results of one call never land on another
+// call's counters; the chunk results follow them.
+constexpr size_t kCounterBytes = (size_t)65536 * sizeof(uint32_t);
+
+static size_t verify_results_bytes(int batch, int gamma, int V) {
   const size_t ch = (size_t)verify_chunks(V);
   const size_t greedy = (size_t)batch * ((size_t)gamma + 1) * ch * sizeof(ArgMax);
-  const size_t reject = (size_t)batch * ch * (2 * sizeof(uint64_t) + sizeof(ArgMax)) + (size_t)batch * sizeof(int32_t);
-  return (greedy > reject ? greedy : reject) + 256;
+  const size_t reject = (size_t)batch * ch * (2 * sizeof(uint64_t) + sizeof(ArgMax));
+  return greedy > reject ? greedy : reject;
+}
+
+extern "C" size_t svlm_verify_workspace(int batch, int gamma, int V) {
+  if (batch < 1 || gamma < 1 || V < 1 || !verify_fits(batch, gamma, V)) return 0;
+  return kCounterBytes + verify_results_bytes(batch, gamma, V);
 }
 
 extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t* draft_tok, const float* target,
@@ -424,17 +451,16 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
   a.u = u;
   a.n_accept = n_accept;
   a.next_tok = next_tok;
-  a.g_part = (ArgMax*)ws;
-  a.r_mass = (uint64_t*)ws;
-  a.r_arg = (ArgMax*)((uint64_t*)ws + (size_t)batch * a.chunks * 2);
-  a.r_first = (int32_t*)(a.r_arg + (size_t)batch * a.chunks);
+  a.arrived = (uint32_t*)ws;
+  char* results = (char*)ws + kCounterBytes;
+  a.g_part = (ArgMax*)results;
+  a.r_mass = (uint64_t*)results;
+  a.r_arg = (ArgMax*)((uint64_t*)results + (size_t)batch * a.chunks * 2);
   hipStream_t st = (hipStream_t)stream;
   if (mode == SVLM_VERIFY_GREEDY) {
     greedy_chunks<<<dim3(a.chunks, gamma + 1, batch), kThreads, 0, st>>>(a);
-    greedy_final<<<batch, kThreads, 0, st>>>(a);
   } else {
     reject_chunks<<<dim3(a.chunks, batch), kThreads, 0, st>>>(a);
-    reject_final<<<batch, kThreads, 0, st>>>(a);
   }
   return check_launch("svlm_verify");
 }

@@ -368,7 +368,8 @@ def verify_workspace_bytes(batch, gamma, V) -> int:
 
 def verify(mode: str, draft_tok: torch.Tensor, target: torch.Tensor, draft_prob: torch.Tensor | None = None,
            u: torch.Tensor | None = None, ws: torch.Tensor | None = None):
-    """mode "greedy": target = logits [B][gamma+1][V]; "reject": target = p, draft_prob = q, u [B][gamma+1]."""
+    """mode "greedy": target = logits [B][gamma+1][V]; "reject": target = p, draft_prob = q, u [B][gamma+1].
+    A caller-held `ws` (verify_workspace_bytes) must be zero-filled before its first use."""
     _dev(draft_tok, target, draft_prob, u, ws)
     B, gamma = draft_tok.shape
     V = target.shape[-1]
@@ -388,7 +389,9 @@ def verify(mode: str, draft_tok: torch.Tensor, target: torch.Tensor, draft_prob:
     nxt = torch.empty(B, dtype=torch.int32, device=target.device)
     need = verify_workspace_bytes(B, gamma, V)
     if ws is None:
-        ws = _ws(need, target.device)
+        # the workspace ends in arrival counters that must start at zero (every
+        # call leaves them zero, so a caller-held workspace is cleared only once)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=target.device)
     L.call("svlm_verify", m, B, gamma, V, draft_tok.data_ptr(), target.data_ptr(),
            draft_prob.data_ptr() if draft_prob is not None else None, u.data_ptr() if u is not None else None,
            n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())

@@ -611,11 +611,26 @@ def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
     def select():
         ops.select(srows, c5.frames, c5.gh, c5.gw, c5.top_p, c5.budget)
 
+    # greedy acceptance of a gamma = 9 window over vocabulary 152064 (the
+    # hour-long configuration's acceptance): every row's argmax; the drafts
+    # match the first five, so the walk stops at the sixth; 16 calls per graph
+    gv = c5.gamma_verify
+    V = 152064
+    logits = torch.randn(1, gv + 1, V, generator=g, device=dev, dtype=torch.float32)
+    dtok = torch.randint(0, V, (1, gv), generator=g, device=dev, dtype=torch.int32)
+    dtok[0, :5] = logits[0, :5].argmax(dim=-1).to(torch.int32)
+    ws_a = torch.zeros(ops.verify_workspace_bytes(1, gv, V), dtype=torch.uint8, device=dev)
+
+    def accept_greedy():
+        for _ in range(16):
+            ops.verify("greedy", dtok, logits, ws=ws_a)
+
     out = {}
     row = Hkv * D * 2 * 2
     for name, fn, nbytes, n_calls in (("verify_attn", verify, N * row, layers),
                                       ("draft_attn_indexed", draft, n_draft * row, layers),
-                                      ("select", select, R * (c5.n_vis + c5.budget) * 4, 1)):
+                                      ("select", select, R * (c5.n_vis + c5.budget) * 4, 1),
+                                      ("accept_greedy", accept_greedy, (gv + 1) * V * 4, 16)):
         fn()
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
@@ -639,7 +654,9 @@ def measure_hour_shape(torch, ops, dev, g, steps, layers=8):
     out["verify_attn"]["what"] = "dense verify, 10 queries x 141194 keys, 28 q / 4 KV heads, D 128"
     out["draft_attn_indexed"]["what"] = ("draft, 1 query over per-head lists of 1024 visual + 64 text + 1 rows "
                                          "read in place")
-    del kv, qv, qd
+    out["accept_greedy"]["what"] = ("greedy acceptance, gamma 9, V 152064, one launch per call (16 calls per "
+                                    "graph); bytes = the 10 logit rows, each read once")
+    del kv, qv, qd, logits, ws_a
     torch.cuda.empty_cache()
     # the selection rows themselves: the score of all 28 layers in one call,
     # one row per (layer, KV head), over 141120 visual + 64 text keys

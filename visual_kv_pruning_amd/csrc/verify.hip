@@ -24,7 +24,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
-constexpr int kChunk = kThreads * kPerThread;  // 4096 vocabulary entries per chunk
+constexpr int kChunk = kThreads * kPerThread;  // 4096 vocabulary entries per rejection chunk
+// greedy chunks are 4x longer: (gamma + 1) x chunks workgroups each count in
+// on the sequence's arrival counter, and fewer, longer chunks keep that count
+// (and its device-scope release per workgroup) low while a thread's 64 loads
+// still go out in one round trip
+constexpr int kGreedyPerThread = 64;
+constexpr int kGreedyChunk = kThreads * kGreedyPerThread;  // 16384
 
 struct ArgMax {
   float v;
@@ -119,41 +125,55 @@ __device__ int first_reject_wave(const VerifyArgs& a, int b) {
   return G;
 }
 
-// the last workgroup of sequence b: the waves reduce the chunk results of up
-// to 64 rows at a time (a row per wave in turn), then thread 0 walks them in
-// row order to the first draft that differs from the dense argmax
+// the last workgroup of sequence b, 64 rows of the window at a time: wave w
+// reduces the chunk results of rows w, w + 4, ... (every load of a round
+// issued before any reduction), then wave 0 compares the rows' argmaxes with
+// the drafts (one lane per row, loaded alongside) and the first mismatch, or
+// the bonus row, is the lowest set bit of a ballot
 __device__ void greedy_final(const VerifyArgs& a, int b) {
+  constexpr int kRowsPerWave = 64 / (kThreads / 64);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = a.gamma;
   __shared__ int s_am[64];
   __shared__ int s_done;
-  for (int i0 = 0; i0 <= a.gamma; i0 += 64) {
-    const int rows = min(64, a.gamma + 1 - i0);
-    for (int r = wv; r < rows; r += kThreads / 64) {
-      const int i = i0 + r;
-      ArgMax best = {-INFINITY, 0x7fffffff};
-      for (int c = lane; c < a.chunks; c += 64)
-        best = better(best, a.g_part[((int64_t)b * (a.gamma + 1) + i) * a.chunks + c]);
-      best = wave_argmax(best);
-      if (lane == 0) s_am[r] = (best.i == 0x7fffffff) ? 0 : best.i;  // all entries NaN: token 0
+  for (int i0 = 0; i0 <= G; i0 += 64) {
+    const int rows = min(64, G + 1 - i0);
+    const int dtok = (tid < rows && i0 + tid < G) ? a.draft[(int64_t)b * G + i0 + tid] : 0;
+    ArgMax best[kRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) best[k] = ArgMax{-INFINITY, 0x7fffffff};
+    for (int c0 = 0; c0 < a.chunks; c0 += 64) {
+      const int c = c0 + lane;
+      ArgMax v[kRowsPerWave];
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) {
+        const int r = wv + (kThreads / 64) * k;
+        v[k] = (r < rows && c < a.chunks) ? a.g_part[((int64_t)b * (G + 1) + i0 + r) * a.chunks + c]
+                                          : ArgMax{-INFINITY, 0x7fffffff};
+      }
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) best[k] = better(best[k], v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wv + (kThreads / 64) * k;
+      if (r < rows) {  // wave-uniform
+        const ArgMax m = wave_argmax(best[k]);
+        if (lane == 0) s_am[r] = (m.i == 0x7fffffff) ? 0 : m.i;  // all entries NaN: token 0
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      int done = 0;
-      for (int r = 0; r < rows; ++r) {
-        const int i = i0 + r;
-        const int am = s_am[r];
-        if (i < a.gamma) {
-          const int d = a.draft[(int64_t)b * a.gamma + i];
-          debug_check(d >= 0 && d < a.V, SVLM_DBG_DRAFT_TOKEN);
-        }
-        if (i == a.gamma || a.draft[(int64_t)b * a.gamma + i] != am) {
-          a.n_accept[b] = i;
-          a.next_tok[b] = am;
-          done = 1;
-          break;
-        }
+    if (wv == 0) {
+      const int i = i0 + lane;
+      if (lane < rows && i < G) debug_check(dtok >= 0 && dtok < a.V, SVLM_DBG_DRAFT_TOKEN);
+      const int am = (lane < rows) ? s_am[lane] : 0;
+      const bool stop = lane < rows && (i == G || dtok != am);
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(stop);
+      if (m != 0ull && lane == (int)__builtin_ctzll(m)) {
+        a.n_accept[b] = i;
+        a.next_tok[b] = am;
       }
-      s_done = done;
+      if (lane == 0) s_done = (m != 0ull);
     }
     __syncthreads();
     if (s_done) return;
@@ -163,14 +183,14 @@ __device__ void greedy_final(const VerifyArgs& a, int b) {
 __global__ __launch_bounds__(kThreads) void greedy_chunks(VerifyArgs a) {
   const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const float* row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
-  const int base = c * kChunk;
+  const int base = c * kGreedyChunk;
   // all loads first (indices clamped into the row, so none is conditional), then the reduction
-  float x[kPerThread];
+  float x[kGreedyPerThread];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) x[k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
+  for (int k = 0; k < kGreedyPerThread; ++k) x[k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
   ArgMax best = {-INFINITY, 0x7fffffff};
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
+  for (int k = 0; k < kGreedyPerThread; ++k) {
     const int v = base + k * kThreads + threadIdx.x;
     if (v < a.V) best = better(best, ArgMax{x[k], v});
   }
@@ -401,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
 using namespace svlm;
 
 static int verify_chunks(int V) { return (int)(((int64_t)V + kChunk - 1) / kChunk); }
+static int greedy_chunks_of(int V) { return (int)(((int64_t)V + kGreedyChunk - 1) / kGreedyChunk); }
 
 // the greedy pass is a (chunks, gamma + 1, batch) grid, the rejection pass (chunks, batch)
 static bool verify_fits(int batch, int gamma, int V) {
@@ -414,9 +435,8 @@ static bool verify_fits(int batch, int gamma, int V) {
 constexpr size_t kCounterBytes = (size_t)65536 * sizeof(uint32_t);
 
 static size_t verify_results_bytes(int batch, int gamma, int V) {
-  const size_t ch = (size_t)verify_chunks(V);
-  const size_t greedy = (size_t)batch * ((size_t)gamma + 1) * ch * sizeof(ArgMax);
-  const size_t reject = (size_t)batch * ch * (2 * sizeof(uint64_t) + sizeof(ArgMax));
+  const size_t greedy = (size_t)batch * ((size_t)gamma + 1) * (size_t)greedy_chunks_of(V) * sizeof(ArgMax);
+  const size_t reject = (size_t)batch * (size_t)verify_chunks(V) * (2 * sizeof(uint64_t) + sizeof(ArgMax));
   return greedy > reject ? greedy : reject;
 }
 
@@ -458,6 +478,7 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
   a.r_arg = (ArgMax*)((uint64_t*)results + (size_t)batch * a.chunks * 2);
   hipStream_t st = (hipStream_t)stream;
   if (mode == SVLM_VERIFY_GREEDY) {
+    a.chunks = greedy_chunks_of(V);
     greedy_chunks<<<dim3(a.chunks, gamma + 1, batch), kThreads, 0, st>>>(a);
   } else {
     reject_chunks<<<dim3(a.chunks, batch), kThreads, 0, st>>>(a);

@@ -137,3 +137,18 @@ def test_workspace_reused_across_calls_and_modes():
     # every call left the counters zero
     tail = ws[: 4 * 4].cpu().numpy()
     assert not tail.any()
+
+
+def test_greedy_vocab_past_64_chunks():
+    """A vocabulary of more than 64 greedy chunks (16384 entries each): the
+    final pass takes the chunk results of a row in several rounds."""
+    V, gamma = 1_100_000, 2
+    rng = np.random.default_rng(41)
+    logits = rng.standard_normal((1, gamma + 1, V)).astype(np.float32)
+    logits[0, 1, V - 3] = 9.0      # row maxima in the last round of chunks
+    logits[0, 2, 70 * 16384 // 2] = 9.0
+    d = np.array([[int(np.argmax(logits[0, 0])), V - 3]], np.int32)
+    log(f"verify greedy V={V} gamma={gamma}")
+    n, t = _gpu("greedy", d, logits)
+    rn, rt = oracle.verify_greedy(d, logits)
+    assert np.array_equal(n, rn) and np.array_equal(t, rt) and n[0] == 2

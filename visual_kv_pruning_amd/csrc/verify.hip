@@ -11,7 +11,8 @@
 // result is exact integer arithmetic and independent of reduction order.
 //
 // One launch per call: a chunk pass spread over the vocabulary (argmax per
-// row for greedy; masses and argmax of the row to draw from for rejection);
+// row for greedy; masses and argmax of the row to draw from for rejection,
+// with every candidate row's chunk loaded up front on windows of up to 9);
 // the last workgroup of a sequence to finish its chunk (an arrival counter
 // per sequence in the workspace) then reduces the chunk results in chunk
 // order and, for rejection, walks the one chunk where the inverse CDF lands.
@@ -30,6 +31,11 @@ constexpr int kChunk = kThreads * kPerThread;  // 4096 vocabulary entries per re
 // (and its device-scope release per workgroup) low while a thread's 64 loads
 // still go out in one round trip
 constexpr int kGreedyPerThread = 64;
+// rejection windows of at most kPfMaxGamma drafts load every candidate row's
+// chunk at once: 1024-entry chunks keep those (2 gamma + 1) x 4 values per
+// thread in registers
+constexpr int kPfMaxGamma = 9;
+constexpr int kPfPerThread = 4;
 constexpr int kGreedyChunk = kThreads * kGreedyPerThread;  // 16384
 
 struct ArgMax {
@@ -209,7 +215,9 @@ __global__ __launch_bounds__(kThreads) void greedy_chunks(VerifyArgs a) {
 // the last workgroup of sequence b (first rejection at n, or n == gamma):
 // row totals over the chunk results, the chunk where the inverse CDF with
 // uniform uu lands, then that chunk walked in index order
+template <int PT>
 __device__ void reject_final(const VerifyArgs& a, int b, int n, double uu) {
+  constexpr int kCh = kThreads * PT;  // vocabulary entries per chunk
   const int G = a.gamma;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -308,20 +316,20 @@ __device__ void reject_final(const VerifyArgs& a, int b, int n, double uu) {
     }
     return;
   }
-  // walk the chosen chunk in index order: thread t owns [base + 16t, base + 16t + 16)
+  // walk the chosen chunk in index order: thread t owns [base + PT t, base + PT t + PT)
   const float* prow = a.target + ((int64_t)b * (G + 1) + n) * a.V;
   const float* qrow = (n < G && mode == 0) ? a.q + ((int64_t)b * G + n) * a.V : nullptr;
-  const int base = sm_chunk * kChunk + tid * kPerThread;
-  float w[kPerThread], qv[kPerThread];
+  const int base = sm_chunk * kCh + tid * PT;
+  float w[PT], qv[PT];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {  // loads first, indices clamped into the row
+  for (int k = 0; k < PT; ++k) {  // loads first, indices clamped into the row
     const int v = min(base + k, a.V - 1);
     w[k] = prow[v];
     qv[k] = qrow ? qrow[v] : 0.f;
   }
   uint64_t mine = 0;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
+  for (int k = 0; k < PT; ++k) {
     const float p = w[k];
     const float x = (base + k < a.V) ? (qrow ? fmaxf(p - qv[k], 0.f) : p) : 0.f;
     w[k] = x;
@@ -342,8 +350,8 @@ __device__ void reject_final(const VerifyArgs& a, int b, int n, double uu) {
   const uint64_t tc = sm_t;  // target offset inside the chosen chunk
   if (mine > 0 && excl <= tc && tc < excl + mine) {
     uint64_t cum = excl;
-    int tok = base + kPerThread - 1;
-    for (int k = 0; k < kPerThread; ++k) {
+    int tok = base + PT - 1;
+    for (int k = 0; k < PT; ++k) {
       cum += mass40(w[k]);
       if (cum > tc) { tok = base + k; break; }
     }
@@ -353,36 +361,20 @@ __device__ void reject_final(const VerifyArgs& a, int b, int n, double uu) {
 }
 
 
-__global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
-  const int c = blockIdx.x, b = blockIdx.y;
-  __shared__ int sm_n;
-  if (threadIdx.x < 64) {
-    const int n0 = first_reject_wave(a, b);
-    if (threadIdx.x == 0) sm_n = n0;
-  }
-  __syncthreads();
-  const int n = sm_n;
-  const int G = a.gamma;
-  const double uu = a.u[(int64_t)b * (G + 1) + G];  // the draw's uniform, used by the last workgroup
-  const float* prow = a.target + ((int64_t)b * (G + 1) + n) * a.V;
-  const float* qrow = (n < G) ? a.q + ((int64_t)b * G + n) * a.V : nullptr;
-  const int base = c * kChunk;
-  // all loads first (indices clamped into the row, so none is conditional), then the sums
-  float pv[kPerThread], qv[kPerThread];
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int v = min(base + k * kThreads + (int)threadIdx.x, a.V - 1);
-    pv[k] = prow[v];
-    qv[k] = qrow ? qrow[v] : 0.f;
-  }
+// The chunk's masses (residual row or bonus row, the fallback row p) and
+// argmax of p, stored by thread 0 for the last workgroup.
+template <int PT>
+__device__ __forceinline__ void reject_chunk_masses(const VerifyArgs& a, int b, int c, bool has_q,
+                                                    const float (&pv)[PT], const float (&qv)[PT]) {
+  const int base = c * kThreads * PT;
   uint64_t mw = 0, mp = 0;
   ArgMax best = {-INFINITY, 0x7fffffff};
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
+  for (int k = 0; k < PT; ++k) {
     const int v = base + k * kThreads + threadIdx.x;
     if (v < a.V) {
       const float p = pv[k];
-      const float w = qrow ? fmaxf(p - qv[k], 0.f) : p;
+      const float w = has_q ? fmaxf(p - qv[k], 0.f) : p;
       mw += mass40(w);
       mp += mass40(p);
       best = better(best, ArgMax{p, v});
@@ -412,7 +404,108 @@ __global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
     a.r_mass[((int64_t)b * a.chunks + c) * 2 + 1] = tp;
     a.r_arg[(int64_t)b * a.chunks + c] = r;
   }
-  if (arrive_last(a, b, (uint32_t)a.chunks)) reject_final(a, b, n, uu);
+}
+
+// Any window: the first rejection n first, then the chunk of row n (p_n and
+// q_n, or the bonus row p_gamma).
+__global__ __launch_bounds__(kThreads) void reject_chunks(VerifyArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  __shared__ int sm_n;
+  if (threadIdx.x < 64) {
+    const int n0 = first_reject_wave(a, b);
+    if (threadIdx.x == 0) sm_n = n0;
+  }
+  __syncthreads();
+  const int n = sm_n;
+  const int G = a.gamma;
+  const double uu = a.u[(int64_t)b * (G + 1) + G];  // the draw's uniform, used by the last workgroup
+  const float* prow = a.target + ((int64_t)b * (G + 1) + n) * a.V;
+  const float* qrow = (n < G) ? a.q + ((int64_t)b * G + n) * a.V : nullptr;
+  const int base = c * kChunk;
+  // all loads first (indices clamped into the row, so none is conditional), then the sums
+  float pv[kPerThread], qv[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int v = min(base + k * kThreads + (int)threadIdx.x, a.V - 1);
+    pv[k] = prow[v];
+    qv[k] = qrow ? qrow[v] : 0.f;
+  }
+  reject_chunk_masses<kPerThread>(a, b, c, qrow != nullptr, pv, qv);
+  if (arrive_last(a, b, (uint32_t)a.chunks)) reject_final<kPerThread>(a, b, n, uu);
+}
+
+// Windows of at most GMAX drafts: the chunk of every row the draw could take
+// (p_0 .. p_gamma and q_0 .. q_gamma-1) is loaded while the first rejection
+// is found, so the row's values are in registers when n is known.  One memory
+// round trip less than the generic form, for 2 gamma + 1 rows read instead of
+// two.  Wave 0's draft tokens and uniforms are loaded before the rows, so its
+// wait for them does not wait for the rows (loads complete in issue order).
+template <int GMAX>
+__global__ __launch_bounds__(kThreads) void reject_chunks_pf(VerifyArgs a) {
+  constexpr int PT = kPfPerThread;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int G = a.gamma;  // <= GMAX
+  const int lane = threadIdx.x & 63;
+  __shared__ int sm_n;
+  int dtok = 0;
+  double ui = 0.0;
+  if (threadIdx.x < 64 && lane < G) {
+    dtok = a.draft[(int64_t)b * G + lane];
+    ui = a.u[(int64_t)b * (G + 1) + lane];
+  }
+  const double uu = a.u[(int64_t)b * (G + 1) + G];
+  const int base = c * kThreads * PT;
+  float pv[GMAX + 1][PT], qv[GMAX][PT];
+#pragma unroll
+  for (int r = 0; r <= GMAX; ++r) {
+    if (r <= G) {
+      const float* row = a.target + ((int64_t)b * (G + 1) + r) * a.V;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) pv[r][k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < GMAX; ++r) {
+    if (r < G) {
+      const float* row = a.q + ((int64_t)b * G + r) * a.V;
+#pragma unroll
+      for (int k = 0; k < PT; ++k) qv[r][k] = row[min(base + k * kThreads + (int)threadIdx.x, a.V - 1)];
+    }
+  }
+  if (threadIdx.x < 64) {
+    bool rej = false;
+    if (lane < G) {
+      const int d = clamp_tok(dtok, a.V);
+      const double pd = a.target[((int64_t)b * (G + 1) + lane) * a.V + d];
+      const double qd = a.q[((int64_t)b * G + lane) * a.V + d];
+      debug_check(pd >= 0.0 && pd <= 1.0 && qd >= 0.0 && qd <= 1.0, SVLM_DBG_PROB_RANGE);
+      rej = !(ui * qd <= pd);
+    }
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(rej);
+    if (threadIdx.x == 0) sm_n = (m != 0ull) ? (int)__builtin_ctzll(m) : G;
+  }
+  __syncthreads();
+  const int n = sm_n;
+  float ps[PT], qs[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    ps[k] = 0.f;
+    qs[k] = 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r <= GMAX; ++r)
+    if (r == n) {  // uniform
+#pragma unroll
+      for (int k = 0; k < PT; ++k) ps[k] = pv[r][k];
+    }
+#pragma unroll
+  for (int r = 0; r < GMAX; ++r)
+    if (r == n) {
+#pragma unroll
+      for (int k = 0; k < PT; ++k) qs[k] = qv[r][k];
+    }
+  reject_chunk_masses<PT>(a, b, c, n < G, ps, qs);
+  if (arrive_last(a, b, (uint32_t)a.chunks)) reject_final<PT>(a, b, n, uu);
 }
 
 }  // namespace
@@ -422,10 +515,12 @@ using namespace svlm;
 
 static int verify_chunks(int V) { return (int)(((int64_t)V + kChunk - 1) / kChunk); }
 static int greedy_chunks_of(int V) { return (int)(((int64_t)V + kGreedyChunk - 1) / kGreedyChunk); }
+static int pf_chunks(int V) { return (int)(((int64_t)V + kThreads * kPfPerThread - 1) / (kThreads * kPfPerThread)); }
 
-// the greedy pass is a (chunks, gamma + 1, batch) grid, the rejection pass (chunks, batch)
+// the greedy pass is a (chunks, gamma + 1, batch) grid, the rejection pass
+// (chunks, batch); the prefetching rejection form has the most chunks
 static bool verify_fits(int batch, int gamma, int V) {
-  return grid_fits(verify_chunks(V), kThreads, (int64_t)gamma + 1, batch);
+  return grid_fits(pf_chunks(V), kThreads, (int64_t)gamma + 1, batch);
 }
 
 // The workspace opens with one arrival counter per possible sequence (the
@@ -436,7 +531,8 @@ constexpr size_t kCounterBytes = (size_t)65536 * sizeof(uint32_t);
 
 static size_t verify_results_bytes(int batch, int gamma, int V) {
   const size_t greedy = (size_t)batch * ((size_t)gamma + 1) * (size_t)greedy_chunks_of(V) * sizeof(ArgMax);
-  const size_t reject = (size_t)batch * (size_t)verify_chunks(V) * (2 * sizeof(uint64_t) + sizeof(ArgMax));
+  // rejection: the prefetching form's shorter chunks (the larger count)
+  const size_t reject = (size_t)batch * (size_t)pf_chunks(V) * (2 * sizeof(uint64_t) + sizeof(ArgMax));
   return greedy > reject ? greedy : reject;
 }
 
@@ -464,7 +560,8 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
   a.batch = batch;
   a.gamma = gamma;
   a.V = V;
-  a.chunks = verify_chunks(V);
+  // chunk count of the form that runs
+  a.chunks = (mode == SVLM_VERIFY_GREEDY) ? greedy_chunks_of(V) : (gamma <= kPfMaxGamma) ? pf_chunks(V) : verify_chunks(V);
   a.draft = draft_tok;
   a.target = target;
   a.q = draft_prob;
@@ -477,12 +574,12 @@ extern "C" int svlm_verify(int mode, int batch, int gamma, int V, const int32_t*
   a.r_mass = (uint64_t*)results;
   a.r_arg = (ArgMax*)((uint64_t*)results + (size_t)batch * a.chunks * 2);
   hipStream_t st = (hipStream_t)stream;
-  if (mode == SVLM_VERIFY_GREEDY) {
-    a.chunks = greedy_chunks_of(V);
+  if (mode == SVLM_VERIFY_GREEDY)
     greedy_chunks<<<dim3(a.chunks, gamma + 1, batch), kThreads, 0, st>>>(a);
-  } else {
+  else if (gamma <= kPfMaxGamma)
+    reject_chunks_pf<kPfMaxGamma><<<dim3(a.chunks, batch), kThreads, 0, st>>>(a);
+  else
     reject_chunks<<<dim3(a.chunks, batch), kThreads, 0, st>>>(a);
-  }
   return check_launch("svlm_verify");
 }
 

@@ -344,11 +344,12 @@ def main():
         flop=score_flop, tflops=round(score_flop / (per_us["score_layer_calls"] * 1e-6) / 1e12, 1),
         what="the same score as 80 svlm_score calls (one per layer, accumulated with alpha/beta)")
     # acceptance: the gamma test probabilities, then the one row (p_n and q_n, or the bonus row p_gamma)
-    # the draw scans; latency-bound (two launches, dependent loads)
+    # the draw scans; latency-bound (one launch, dependent loads).  The kernel reads every candidate
+    # row's chunk up front to save a round trip; the algorithmic bytes are the two rows the draw needs
     acc_bytes = 2 * V * 4
     kernels["accept"].update(bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept"] * 1e-6) / 1e9, 1),
                              what="rejection acceptance, gamma 5, V 152064: bytes = the two probability rows "
-                                  "the draw reads (p_n and q_n); one launch of dependent loads")
+                                  "the draw needs (p_n and q_n); one launch of dependent loads")
     kernels["accept_in_sequence"].update(
         bytes=acc_bytes, gbs=round(acc_bytes / (per_us["accept_in_sequence"] * 1e-6) / 1e9, 1),
         what="the same acceptance call, 16 calls in one graph (per call)")

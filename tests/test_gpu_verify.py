@@ -152,3 +152,40 @@ def test_greedy_vocab_past_64_chunks():
     n, t = _gpu("greedy", d, logits)
     rn, rt = oracle.verify_greedy(d, logits)
     assert np.array_equal(n, rn) and np.array_equal(t, rt) and n[0] == 2
+
+
+@pytest.mark.parametrize("mode", ["reject", "greedy"])
+def test_graph_replays_reset_the_counters(mode):
+    """The call captured once in a HIP graph and replayed on new inputs (copied
+    in eagerly between replays): every replay's arrival counters start at zero
+    because the previous replay's last workgroups reset them."""
+    from visual_kv_pruning_amd import ops
+    V, gamma, B = 152064, (5 if mode == "reject" else 9), 2
+    ws = torch.zeros(ops.verify_workspace_bytes(B, gamma, V), dtype=torch.uint8, device="cuda:0")
+    vi0 = W.verify_inputs(60, B, gamma, V, extra=V)
+    d_t = _t(vi0.draft_tok_sampled if mode == "reject" else vi0.draft_tok_greedy, np.int32)
+    t_t = _t(vi0.p if mode == "reject" else vi0.target_logits, np.float32)
+    q_t = _t(vi0.q, np.float32) if mode == "reject" else None
+    u_t = _t(vi0.u, np.float32) if mode == "reject" else None
+    ops.verify(mode, d_t, t_t, q_t, u_t, ws=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        n_out, t_out = ops.verify(mode, d_t, t_t, q_t, u_t, ws=ws)
+    for rep in range(4):
+        vi = W.verify_inputs(61 + rep, B, gamma, V, extra=V)
+        if mode == "reject":
+            d = vi.draft_tok_sampled
+            d_t.copy_(_t(d, np.int32)); t_t.copy_(_t(vi.p, np.float32))
+            q_t.copy_(_t(vi.q, np.float32)); u_t.copy_(_t(vi.u, np.float32))
+            rn, rt = oracle.verify_reject(d, vi.p, vi.q, vi.u)
+        else:
+            d = vi.draft_tok_greedy.copy()
+            d[:, : rep + 1] = np.argmax(vi.target_logits[:, : rep + 1], axis=-1)
+            d_t.copy_(_t(d, np.int32)); t_t.copy_(_t(vi.target_logits, np.float32))
+            rn, rt = oracle.verify_greedy(d, vi.target_logits)
+        log(f"verify graph replay mode={mode} rep={rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(n_out.cpu().numpy(), rn) and np.array_equal(t_out.cpu().numpy(), rt)
+    assert not ws[: 4 * B].cpu().numpy().any()

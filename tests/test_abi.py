@@ -72,6 +72,21 @@ def test_split_select_plan(lib):
     assert lib.svlm_verify_workspace(0, 5, 10) == 0
 
 
+def test_verify_workspace_layout(lib):
+    """The acceptance workspace opens with 256 KB of arrival counters (one per
+    sequence index, the same place for every call shape), then the chunk
+    results of the larger of the two forms: greedy 8 bytes per (row, 16384
+    vocabulary entries), rejection 24 bytes per 1024 entries."""
+    def expect(batch, gamma, V):
+        greedy = batch * (gamma + 1) * (-(-V // 16384)) * 8
+        reject = batch * (-(-V // 1024)) * 24
+        return 256 * 1024 + max(greedy, reject)
+    for batch, gamma, V in ((1, 5, 152064), (4, 9, 152064), (3, 70, 5000), (1, 1, 1), (2, 63, 1_100_000)):
+        assert lib.svlm_verify_workspace(batch, gamma, V) == expect(batch, gamma, V)
+    # every shape of a smaller call fits the workspace of a larger one
+    assert lib.svlm_verify_workspace(1, 5, 152064) <= lib.svlm_verify_workspace(4, 9, 152064)
+
+
 NULL = None
 
 

@@ -190,6 +190,21 @@ def test_llava72b_shape_verify_and_draft_full_size():
     _check(q[:, :1], k[:, :nk], v[:, :nk], [nk], False, name="72B draft")
 
 
+@pytest.mark.parametrize("cfg", [W.C2, W.C4], ids=lambda c: c.name)
+def test_qwen_shapes_verify_and_draft_full_size(cfg):
+    """The Qwen2-VL-7B (28 q / 4 KV heads, 8266 verify keys, two row chunks)
+    and Qwen2.5-VL-32B (40 q / 8 KV heads, 20842 verify keys, one chunk of
+    four row blocks) shapes at full size, every head, as the bench times them:
+    dense verify of gamma + 1 = 10 queries and the 10% draft."""
+    nq = cfg.gamma_verify + 1
+    N = cfg.n_ctx + nq
+    k, v = W.random_kv(cfg.index, cfg.hkv, N, cfg.d, layer=0)
+    q = W.decode_queries(cfg, 0, nq)
+    _check(q, k, v, [N], True, name=f"{cfg.name} verify")
+    nk = cfg.budget + cfg.n_text + 1
+    _check(q[:, :1], k[:, :nk], v[:, :nk], [nk], False, name=f"{cfg.name} draft")
+
+
 def test_hour_long_shape_verify_sampled_heads():
     """141,194-key dense verify at the hour-long shape; oracle on the first KV head's rows."""
     cfg = W.C5

@@ -47,7 +47,10 @@ def test_greedy_ties_take_lowest_index():
     assert (n[0], t[0]) == (2, 100)
 
 
-@pytest.mark.parametrize("vocab,gamma,batch", [(1024, 4, 4), (152064, 9, 2), (152064, 5, 1), (777, 2, 3)])
+# gamma <= 9 takes the form that loads every candidate row up front; 10 and
+# 16 the form that reads row n after finding it
+@pytest.mark.parametrize("vocab,gamma,batch", [(1024, 4, 4), (152064, 9, 2), (152064, 5, 1), (777, 2, 3),
+                                               (152064, 10, 2), (5000, 16, 3)])
 @pytest.mark.parametrize("seed", range(6))
 def test_reject_bit_exact(vocab, gamma, batch, seed):
     vi = W.verify_inputs(20 + seed, batch, gamma, vocab, extra=vocab)

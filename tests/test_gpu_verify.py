@@ -192,3 +192,30 @@ def test_graph_replays_reset_the_counters(mode):
         torch.cuda.synchronize()
         assert np.array_equal(n_out.cpu().numpy(), rn) and np.array_equal(t_out.cpu().numpy(), rt)
     assert not ws[: 4 * B].cpu().numpy().any()
+
+
+def test_seeded_random_shapes_both_modes():
+    """40 seeded random calls of either mode: batch 1-5, window 1-20 (both
+    rejection forms), vocabularies from 1 to 200000 (chunk counts of 1 to
+    over 100, ragged last chunks), uniforms scaled so that accepted runs are
+    short or long; each bit-exact against the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        mode = "reject" if case % 2 == 0 else "greedy"
+        batch = int(rng.integers(1, 6))
+        gamma = int(rng.integers(1, 21))
+        V = int(rng.choice([1, 3, 1000, 1024, 1025, 4097, 16383, 16385, 65536, 152064, 200000]))
+        vi = W.verify_inputs(100 + case, batch, gamma, V, extra=V)
+        log(f"verify random case {case}: mode={mode} B={batch} gamma={gamma} V={V}")
+        if mode == "reject":
+            u = vi.u.copy()
+            u[:, :gamma] *= np.float32(rng.choice([1.0, 0.2, 0.01]))
+            n, t = _gpu("reject", vi.draft_tok_sampled, vi.p, vi.q, u)
+            rn, rt = oracle.verify_reject(vi.draft_tok_sampled, vi.p, vi.q, u)
+        else:
+            d = vi.draft_tok_greedy.copy()
+            k = int(rng.integers(0, gamma + 1))
+            d[:, :k] = np.argmax(vi.target_logits[:, :k], axis=-1)
+            n, t = _gpu("greedy", d, vi.target_logits)
+            rn, rt = oracle.verify_greedy(d, vi.target_logits)
+        assert np.array_equal(n, rn) and np.array_equal(t, rt), f"case {case}"
